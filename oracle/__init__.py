@@ -1,0 +1,34 @@
+"""CPU fp64 oracle of the forward-attention path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import or call this
+package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP path.
+
+What it computes is the plain definition of scaled-dot-product attention,
+materialised in full for every query row: logits x = scale * q.k (or the MLA
+logit with per-token scales), masked keys at -inf, P = softmax over keys, and
+O = P.V, with LSE = log sum exp of the row.  The pages (Modular's Mojo kernel
+docs: "KVPipelineGeneric", "MLASmemStorage", AMD attention "buffers") name the
+two contractions S = Q.K^T and O += P.V, a per-row correction buffer (the
+online-softmax rescale) and the nope/rope + q_scale/k_scale split of MLA; they
+never print the softmax, so the textbook definition stands in for it.  The
+oracle never blocks over keys (that would be the online algorithm it checks).
+
+parity pins: see tests/test_oracle_*.py (brute force, torch CPU fp64 SDPA,
+closed forms, invariants, the OCP e4m3 code table).
+"""
+from .codecs import bf16_to_f64, e4m3_to_f64, E4M3_TABLE
+from .attention import (
+    sdpa_rows,
+    prefill,
+    prefill_rows,
+    decode,
+    mla_prefill,
+    mla_prefill_rows,
+    mla_decode,
+)
+
+__all__ = [
+    "bf16_to_f64", "e4m3_to_f64", "E4M3_TABLE",
+    "sdpa_rows", "prefill", "prefill_rows", "decode", "mla_prefill", "mla_prefill_rows", "mla_decode",
+]
