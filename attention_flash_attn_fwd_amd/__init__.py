@@ -1,0 +1,187 @@
+"""Python binding of libattn.so, the gfx950 forward-attention library.
+
+Argument marshalling only: every step of attention runs in the HIP kernels behind
+the C ABI declared in include/attn.h.  PyTorch supplies device memory (outputs and
+workspaces are allocated with torch) and the current HIP stream.  If libattn.so is
+missing, every call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+
+EXPORTS = {
+    "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 8 +
+                         [ctypes.c_float, ctypes.c_void_p]),
+    "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "attn_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 +
+                        [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "mla_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10 +
+                        [ctypes.c_float, ctypes.c_void_p]),
+    "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "mla_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
+                       [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with attention_flash_attn_fwd_amd.build.build()")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            f = getattr(l, name)
+            f.restype, f.argtypes = res, args
+        _lib = l
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise AttnError(fn, status)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None, return_lse: bool = False):
+    """Flash-attention forward.  q [B,Sq,Hq,D], k/v [B,Skv,Hkv,D] (bf16 or fp32) -> o [B,Sq,Hq,D]."""
+    dts = (torch.bfloat16, torch.float32)
+    _need(q, "q", dts, 4); _need(k, "k", (q.dtype,), 4); _need(v, "v", (q.dtype,), 4)
+    B, Sq, Hq, D = q.shape
+    Skv, Hkv = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    dt = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
+    st = lib().attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dt, B, Sq, Skv, Hq, Hkv, D,
+                                int(bool(causal)), scale, _stream())
+    _check("attn_prefill_fwd", st)
+    return (o, lse) if return_lse else o
+
+
+def decode_workspace_size(B: int, Hq: int, D: int, max_kv_len: int) -> int:
+    return int(lib().attn_decode_workspace_size(B, Hq, D, max_kv_len))
+
+
+def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=None, out=None,
+           return_lse: bool = False):
+    """Decode: q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D] bf16, kv_lens int32 [B] (device) -> o [B,Hq,D]."""
+    _need(q, "q", (torch.bfloat16,), 3); _need(k_cache, "k_cache", (torch.bfloat16,), 4)
+    _need(v_cache, "v_cache", (torch.bfloat16,), 4); _need(kv_lens, "kv_lens", (torch.int32,), 1)
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != D or v_cache.shape != k_cache.shape or kv_lens.shape[0] != B:
+        raise ValueError("shape mismatch")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    need = decode_workspace_size(B, Hq, D, Lmax)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib().attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(kv_lens), ATTN_BF16,
+                               B, Hq, Hkv, D, Lmax, scale, _ptr(workspace), workspace.numel(), _stream())
+    _check("attn_decode_fwd", st)
+    return (o, lse) if return_lse else o
+
+
+def mla_prefill(q_nope, q_rope, k_nope, k_rope, v, q_scale=None, k_scale=None, causal: bool = True,
+                scale: float | None = None, out=None, return_lse: bool = False):
+    """MLA prefill.  q_nope/k_nope [B,S,H,128] e4m3 (uint8 codes or float8_e4m3fn) or bf16;
+    q_rope [B,Sq,H,64], k_rope [B,Skv,Hr,64], v [B,Skv,H,128] bf16; q_scale [B,Sq,H], k_scale [B,Skv,H] fp32."""
+    fp8 = q_nope.dtype in _FP8
+    ndt = _FP8 if fp8 else (torch.bfloat16,)
+    _need(q_nope, "q_nope", ndt, 4); _need(k_nope, "k_nope", ndt, 4)
+    _need(q_rope, "q_rope", (torch.bfloat16,), 4); _need(k_rope, "k_rope", (torch.bfloat16,), 4)
+    _need(v, "v", (torch.bfloat16,), 4)
+    B, Sq, H, Dn = q_nope.shape
+    Skv, Dr, Hr, Dv = k_nope.shape[1], q_rope.shape[3], k_rope.shape[2], v.shape[3]
+    for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale")):
+        if t is not None:
+            _need(t, n, (torch.float32,), 3)
+    if q_scale is not None and tuple(q_scale.shape) != (B, Sq, H):
+        raise ValueError("q_scale shape")
+    if k_scale is not None and tuple(k_scale.shape) != (B, Skv, H):
+        raise ValueError("k_scale shape")
+    if (tuple(k_nope.shape) != (B, Skv, H, Dn) or tuple(q_rope.shape[:3]) != (B, Sq, H)
+            or tuple(k_rope.shape) != (B, Skv, Hr, Dr) or tuple(v.shape[:3]) != (B, Skv, H)):
+        raise ValueError("shape mismatch")
+    scale = 1.0 / math.sqrt(Dn + Dr) if scale is None else float(scale)
+    o = torch.empty((B, Sq, H, Dv), dtype=torch.bfloat16, device=v.device) if out is None else out
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device=v.device) if return_lse else None
+    st = lib().mla_prefill_fwd(_ptr(q_nope), _ptr(q_rope), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(o),
+                               _ptr(q_scale), _ptr(k_scale), _ptr(lse), ATTN_FP8_E4M3 if fp8 else ATTN_BF16,
+                               B, Sq, Skv, H, Hr, Dn, Dr, Dv, int(bool(causal)), scale, _stream())
+    _check("mla_prefill_fwd", st)
+    return (o, lse) if return_lse else o
+
+
+def mla_decode_workspace_size(B: int, H: int, Dv: int, max_kv_len: int) -> int:
+    return int(lib().mla_decode_workspace_size(B, H, Dv, max_kv_len))
+
+
+def mla_decode(q, kv_cache, kv_lens, dv: int = 512, scale: float | None = None, workspace=None, out=None,
+               return_lse: bool = False):
+    """MLA decode: q [B,H,Dk] bf16, latent cache [B,Lmax,Dk] bf16 (V = first dv columns) -> o [B,H,dv]."""
+    _need(q, "q", (torch.bfloat16,), 3); _need(kv_cache, "kv_cache", (torch.bfloat16,), 3)
+    _need(kv_lens, "kv_lens", (torch.int32,), 1)
+    B, H, Dk = q.shape
+    Lmax = kv_cache.shape[1]
+    if kv_cache.shape[0] != B or kv_cache.shape[2] != Dk or kv_lens.shape[0] != B:
+        raise ValueError("shape mismatch")
+    scale = 1.0 / math.sqrt(Dk) if scale is None else float(scale)
+    need = mla_decode_workspace_size(B, H, dv, Lmax)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib().mla_decode_fwd(_ptr(q), _ptr(kv_cache), _ptr(o), _ptr(lse), _ptr(kv_lens), B, H, Dk, dv, Lmax,
+                              scale, _ptr(workspace), workspace.numel(), _stream())
+    _check("mla_decode_fwd", st)
+    return (o, lse) if return_lse else o

@@ -1,0 +1,146 @@
+// C ABI of libattn.so: argument validation (host only, before any HIP call) and dispatch
+// to the kernel launchers.  Declarations and contracts: include/attn.h.
+#include "attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool bad_scale(float s) { return !(std::isfinite(s) && s > 0.f); }
+
+// product of non-negative sizes, or -1 on overflow past kMaxElems
+int64_t elems(std::initializer_list<int64_t> dims) {
+  int64_t n = 1;
+  for (int64_t d : dims) {
+    if (d < 0) return -1;
+    if (d != 0 && n > kMaxElems / d) return -1;
+    n *= d;
+  }
+  return n;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (negative size, Hq % Hkv != 0, or too large)";
+    case ATTN_ERR_DTYPE: return "dtype not supported by this entry point";
+    case ATTN_ERR_UNSUPPORTED: return "head dims or options outside the supported set";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+    case ATTN_ERR_SCALE: return "softmax_scale must be finite and positive";
+    default: return "unknown status";
+  }
+}
+
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int B, int Sq,
+                     int Skv, int Hq, int Hkv, int D, int causal, float softmax_scale, hipStream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (B < 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (elems({B, Sq, Hq, D}) < 0 || elems({B, Skv, Hkv, D}) < 0) return ATTN_ERR_SHAPE;
+  if (elems({(Sq + 127) / 128, B, Hq}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || Sq == 0) return ATTN_OK;
+  if (!q || !o || (Skv > 0 && (!k || !v))) return ATTN_ERR_NULL;
+  fa::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Sq = Sq; a.Skv = Skv; a.Hq = Hq; a.Hkv = Hkv; a.Hr = 1;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale;
+  return hip_status(dtype == ATTN_BF16 ? fa::launch_prefill_bf16(a, D, stream) : fa::launch_prefill_f32(a, D, stream));
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int D, int max_kv_len) {
+  if (B < 0 || Hq <= 0 || D <= 0 || max_kv_len < 0) return 0;
+  const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);
+  return fa::decode_workspace_bytes(B, Hq, D, p.n_split);
+}
+
+int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                    const int32_t* kv_lens, int dtype, int B, int Hq, int Hkv, int D, int max_kv_len,
+                    float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (elems({B, max_kv_len, Hkv, D}) < 0 || elems({B, Hq, D}) < 0) return ATTN_ERR_SHAPE;
+  if (D != 128 || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
+  if (B == 0) return ATTN_OK;
+  if (!q || !o || !kv_lens || (max_kv_len > 0 && (!k_cache || !v_cache))) return ATTN_ERR_NULL;
+  const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);
+  if (B > 65535 || Hkv > 65535 || elems({p.n_split, Hkv, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  const size_t need = fa::decode_workspace_bytes(B, Hq, D, p.n_split);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  fa::DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_lens = kv_lens;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + ((size_t)B * Hq * p.n_split * D * 4 + 255) / 256 * 256);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_kv_len;
+  a.n_split = p.n_split; a.chunk = p.chunk;
+  a.scale = softmax_scale;
+  return hip_status(fa::launch_gqa_decode(a, stream));
+}
+
+int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope, const void* k_rope, const void* v,
+                    void* o, const float* q_scale, const float* k_scale, float* lse, int nope_dtype, int B, int Sq,
+                    int Skv, int H, int Hr, int Dn, int Dr, int Dv, int causal, float softmax_scale,
+                    hipStream_t stream) {
+  if (nope_dtype != ATTN_FP8_E4M3 && nope_dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (B < 0 || Sq < 0 || Skv < 0 || H <= 0 || Hr <= 0 || Dn <= 0 || Dr <= 0 || Dv <= 0) return ATTN_ERR_SHAPE;
+  if (Hr != 1 && Hr != H) return ATTN_ERR_SHAPE;
+  if (elems({B, Sq, H, Dn + Dr + Dv}) < 0 || elems({B, Skv, H, Dn + Dr + Dv}) < 0) return ATTN_ERR_SHAPE;
+  if (elems({(Sq + 127) / 128, B, H}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (Dn != 128 || Dr != 64 || Dv != 128) return ATTN_ERR_UNSUPPORTED;
+  if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || Sq == 0) return ATTN_OK;
+  if (!q_nope || !q_rope || !o || (Skv > 0 && (!k_nope || !k_rope || !v))) return ATTN_ERR_NULL;
+  fa::PrefillArgs a{};
+  a.q = q_nope; a.k = k_nope; a.v = v; a.o = o; a.lse = lse;
+  a.q_rope = q_rope; a.k_rope = k_rope; a.q_scale = q_scale; a.k_scale = k_scale;
+  a.B = B; a.Sq = Sq; a.Skv = Skv; a.Hq = H; a.Hkv = H; a.Hr = Hr;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale;
+  return hip_status(fa::launch_mla_prefill(a, nope_dtype == ATTN_FP8_E4M3, stream));
+}
+
+size_t mla_decode_workspace_size(int B, int H, int Dv, int max_kv_len) {
+  if (B < 0 || H <= 0 || Dv <= 0 || max_kv_len < 0) return 0;
+  const fa::SplitPlan p = fa::mla_decode_plan(B, H, max_kv_len);
+  return fa::decode_workspace_bytes(B, H, Dv, p.n_split);
+}
+
+int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, const int32_t* kv_lens, int B, int H,
+                   int Dk, int Dv, int max_kv_len, float softmax_scale, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  if (B < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || max_kv_len < 0 || Dv > Dk) return ATTN_ERR_SHAPE;
+  if (elems({B, max_kv_len, Dk}) < 0 || elems({B, H, Dk}) < 0) return ATTN_ERR_SHAPE;
+  if (Dk != 576 || Dv != 512 || H % 16 != 0 || H > 128) return ATTN_ERR_UNSUPPORTED;
+  if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
+  if (B == 0) return ATTN_OK;
+  if (!q || !o || !kv_lens || (max_kv_len > 0 && !kv_cache)) return ATTN_ERR_NULL;
+  const fa::SplitPlan p = fa::mla_decode_plan(B, H, max_kv_len);
+  if (B > 65535 || elems({p.n_split, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  const size_t need = fa::decode_workspace_bytes(B, H, Dv, p.n_split);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  fa::DecodeArgs a{};
+  a.q = q; a.k = kv_cache; a.v = nullptr; a.o = o; a.lse = lse; a.kv_lens = kv_lens;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + ((size_t)B * H * p.n_split * Dv * 4 + 255) / 256 * 256);
+  a.B = B; a.Hq = H; a.Hkv = 1; a.max_len = max_kv_len;
+  a.n_split = p.n_split; a.chunk = p.chunk;
+  a.scale = softmax_scale;
+  return hip_status(fa::launch_mla_decode(a, stream));
+}
+
+}  // extern "C"

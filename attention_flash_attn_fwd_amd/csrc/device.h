@@ -1,0 +1,180 @@
+// Device building blocks of the gfx950 attention kernels.
+//
+// Operand layouts (CDNA4 MFMA, as measured on gfx950 with single-wave probes):
+//   v_mfma_f32_32x32x16_bf16: A[m][k] lane l holds m = l%32, k = 8*(l/32)+i (i < 8);
+//     B[k][n] lane l holds n = l%32, the same k; C lane l, register v holds
+//     row 8*(v/4) + 4*(l/32) + v%4, column l%32.
+//   v_mfma_f32_16x16x32_bf16: A lane l holds m = l%16, k = 8*(l/16)+i; C lane l, register v
+//     holds row 4*(l/16) + v, column l%16.
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit scales): m/n and C as the 32x32 bf16
+//     form; each lane holds 32 k values.
+//   ds_read_b64_tr_b16: within each 16-lane group, lane i receives element (i%4) of the
+//     8-byte word read by lane 4*e + i/4, for e = 0..3 -- i.e. when lanes 4r..4r+3
+//     address row r (4 consecutive 16-bit columns each), lane i receives column i of
+//     rows 0..3.
+//   global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l (base = M0).
+//
+// Both attention products run transposed: S^T = K.Q^T (K from LDS as A, Q^T from
+// registers as B) and O^T = V^T.P^T (V^T from LDS through transposing reads as A,
+// P^T from registers as B).  Then a lane owns one query column of S^T, P^T and O^T at
+// once, so the softmax row state (max, sum, rescale factor) stays in that lane and only
+// meets the other half-wave holding the same query.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+#define FA_LDS __attribute__((address_space(3)))
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+typedef __attribute__((ext_vector_type(2))) int i32x2_t;
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// ------------------------------------------------------------------ matrix cores
+
+__device__ __forceinline__ f32x16_t mfma32x32x16_bf16(i32x4_t a, i32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32_bf16(i32x4_t a, i32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// e4m3 x e4m3 -> fp32, K = 64, block scales fixed at 2^0 (E8M0 code 127).
+__device__ __forceinline__ f32x16_t mfma32x32x64_e4m3(i32x8_t a, i32x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+__device__ __forceinline__ f32x16_t mfma32x32x2_f32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ LDS access
+
+__device__ __forceinline__ i32x4_t lds_b128(const FA_LDS char* p) {
+  return *(const FA_LDS i32x4_t*)p;
+}
+__device__ __forceinline__ f32x4_t lds_f32x4(const FA_LDS char* p) {
+  return *(const FA_LDS f32x4_t*)p;
+}
+__device__ __forceinline__ i32x2_t lds_tr16(const FA_LDS char* p) {
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p);
+  return __builtin_bit_cast(i32x2_t, v);
+}
+__device__ __forceinline__ i32x4_t cat(i32x2_t a, i32x2_t b) {
+  i32x4_t r;
+  r.x = a.x; r.y = a.y; r.z = b.x; r.w = b.y;
+  return r;
+}
+
+// Direct global -> LDS copy of 16 (or 4) bytes per lane; `lds` must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* g, FA_LDS char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (FA_LDS void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, FA_LDS char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (FA_LDS void*)lds, 4, 0, 0);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that also keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ------------------------------------------------------------------ LDS swizzles
+//
+// K/V tiles live in LDS as rows of keys, 16-byte chunks XOR-permuted per row.  Readers:
+//  * the S^T A operand: 16 consecutive lanes read 16 consecutive rows at one logical
+//    chunk, so the XOR must be one-to-one over those rows' bank phases;
+//  * the transposing V reads: a 16-lane group reads 4 consecutive rows (row % 4 == 0
+//    first) at one 32-byte slab (an aligned chunk pair), so those rows must land on
+//    distinct chunk pairs.
+// With 64 banks x 4 bytes, a 256-byte row starts every row at the same bank: swz256
+// uses a 4-bit XOR, one-to-one over row % 16, with (xor >> 1) distinct over any 4
+// aligned rows.  128-byte (and 1152-byte) rows alternate between two bank halves by
+// parity: swz_half uses a 3-bit XOR of t = (row >> 1) % 8, one-to-one over t, with
+// (xor >> 1) different for t and t + 1 when t is even (rows r and r + 2).
+
+__device__ __forceinline__ uint32_t swz256(uint32_t row) {
+  return ((row & 3u) << 2) | ((row >> 2) & 3u);
+}
+__device__ __forceinline__ uint32_t swz_half(uint32_t row) {
+  uint32_t t = (row >> 1) & 7u;
+  return ((t & 1u) << 1) | ((t >> 1) & 1u) | (t & 4u);
+}
+
+// ------------------------------------------------------------------ lane exchange
+
+__device__ __forceinline__ float bits_f(uint32_t u) { return __uint_as_float(u); }
+
+// max / sum of x over lanes l and l ^ 32
+__device__ __forceinline__ float xor32_max(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  uint32_t a = p[0], b = p[1];
+  return fmaxf(bits_f(a), bits_f(b));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  uint32_t a = p[0], b = p[1];
+  return bits_f(a) + bits_f(b);
+}
+// max / sum of x over lanes l and l ^ 16
+__device__ __forceinline__ float xor16_max(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  uint32_t a = p[0], b = p[1];
+  return fmaxf(bits_f(a), bits_f(b));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  uint32_t a = p[0], b = p[1];
+  return bits_f(a) + bits_f(b);
+}
+
+// ------------------------------------------------------------------ numerics
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ int pack_bf16(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(int, v);
+}
+
+// Online-softmax step for one query row held by a lane pair (l, l ^ 32).
+// Given the tile's row max `mx` (already reduced over the pair) updates the running
+// max m and returns the factor alpha = exp2((m_old - m_new) * c) that rescales the
+// running sum and the O accumulator, and `neg` = -m_new * c to form exp2(s*c + neg).
+// A row that has seen no visible key keeps m = -inf; its exponent base is then 0 so
+// that no inf - inf appears, and alpha = 0.
+struct RowState {
+  float m;   // running max of the raw scores (-inf before the first visible key)
+  float l;   // running sum of exp2((s - m) * c) over this lane's keys
+};
+__device__ __forceinline__ float softmax_rescale(RowState& st, float mx, float c, float& neg) {
+  float m_new = fmaxf(st.m, mx);
+  float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  float alpha = exp2_fast((st.m - m_use) * c);
+  neg = -m_use * c;
+  st.m = m_new;
+  return alpha;
+}
+
+}  // namespace fa

@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct PrefillArgs {
+  const void* q;        // MHA: q; MLA: q_nope
+  const void* k;        // MHA: k; MLA: k_nope
+  const void* v;
+  void* o;
+  float* lse;           // nullable
+  const void* q_rope;   // MLA only
+  const void* k_rope;   // MLA only
+  const float* q_scale; // MLA only, nullable (= 1)
+  const float* k_scale; // MLA only, nullable (= 1)
+  int B, Sq, Skv, Hq, Hkv, Hr;
+  int causal;
+  float scale;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;        // GQA: k cache; MLA: latent cache
+  const void* v;        // GQA: v cache; MLA: unused (V = first Dv columns of k)
+  void* o;
+  float* lse;
+  const int32_t* kv_lens;
+  float* part_o;        // workspace: [B, Hq, n_split, Dv] fp32
+  float* part_ml;       // workspace: [B, Hq, n_split, 2] fp32 (row max, row sum)
+  int B, Hq, Hkv, max_len;
+  int n_split, chunk;   // keys per split
+  float scale;
+};
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t s);
+hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, hipStream_t s);
+
+// Split plan of the decode kernels (host-only arithmetic, shared with the workspace query).
+struct SplitPlan {
+  int chunk;
+  int n_split;
+};
+SplitPlan gqa_decode_plan(int B, int Hq, int max_len);
+SplitPlan mla_decode_plan(int B, int H, int max_len);
+size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split);
+
+hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_mla_decode(const DecodeArgs& a, hipStream_t s);
+
+}  // namespace fa

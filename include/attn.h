@@ -1,0 +1,134 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) forward-attention library (libattn.so).
+ *
+ * What is computed.  Scaled-dot-product attention, forward only:
+ *     x[i,j] = scale * q_i . k_j          (MLA prefill: see mla_prefill_fwd)
+ *     P[i,:] = softmax over the keys j visible to query i
+ *     O[i,:] = sum_j P[i,j] v_j,   LSE[i] = ln sum_j exp(x[i,j])
+ * evaluated as tiled flash attention: S = Q.K^T on a K tile, an online softmax with a
+ * running row max and sum whose per-row correction rescales the O accumulator, then
+ * O += P.V on the matching V tile.  Modular's Mojo kernel pages describe this path:
+ * "KVPipelineGeneric" (NVIDIA sm100, MLA decode utilities; description and Parameters:
+ * the S = Q.K' and O += P.V products pipelined over K/V tiles), "MLASmemStorage" (sm100
+ * per-token-scale MLA prefill; description, Parameters and Fields: Q and K split into
+ * nope and rope parts, a q_scale per Q-tile row and a k_scale per K-tile row, a per-row
+ * correction buffer) and the AMD attention "buffers" module (K/V tile buffers with a
+ * token_gen (decode) variant, Q/P/O operands held in registers).
+ *
+ * Conventions shared by every entry point.
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library never
+ *    allocates, frees or retains memory and keeps no state between calls.
+ *  - Layouts are row-major and contiguous, token-major: q/o [B, Sq, Hq, D],
+ *    k/v [B, Skv, Hkv, D], decode caches [B, max_kv_len, Hkv, D].
+ *  - Query head h reads kv head h / (Hq / Hkv) (consecutive GQA groups).
+ *  - Causal masking is aligned bottom-right: query i sees key j iff j <= i + (Skv - Sq).
+ *    A query row that sees no key gets O = 0 and LSE = -inf.
+ *  - softmax_scale multiplies the logits; it must be finite and > 0.
+ *  - lse (nullable) receives fp32 natural-log LSE, [B, Hq, Sq] (prefill) or [B, Hq] (decode).
+ *  - Every call enqueues its kernels on `stream` (0 = the null stream) and returns
+ *    before they finish; there is no host synchronisation inside the library.
+ *  - Errors: arguments are validated on the host BEFORE any HIP call, and a non-OK
+ *    status is returned with nothing enqueued.  A failed launch returns ATTN_ERR_HIP.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - Concurrent calls are safe; calls that run concurrently need distinct workspaces.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_F32 = 0,       /* IEEE binary32 */
+  ATTN_BF16 = 1,      /* bfloat16 */
+  ATTN_FP8_E4M3 = 2   /* OCP 8-bit e4m3fn: bias 7, max 448, no infinities */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = -1,         /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = -2,        /* a size is negative, or Hq % Hkv != 0, or sizes overflow */
+  ATTN_ERR_DTYPE = -3,        /* dtype not accepted by this entry point */
+  ATTN_ERR_UNSUPPORTED = -4,  /* head dims / options outside the compiled set */
+  ATTN_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than *_workspace_size() */
+  ATTN_ERR_HIP = -6,          /* a HIP launch failed */
+  ATTN_ERR_SCALE = -7         /* softmax_scale not finite and positive */
+} attn_status_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_string(int status);
+
+/*
+ * Prefill / MHA / GQA forward (KVPipelineGeneric page: S = Q.K' then O += P.V over
+ * pipelined K/V tiles; AMD buffers page: Q held in registers, K/V tiles staged in LDS).
+ *   q [B,Sq,Hq,D], k [B,Skv,Hkv,D], v [B,Skv,Hkv,D], o [B,Sq,Hq,D]: all `dtype`
+ *   (ATTN_BF16 or ATTN_F32); bf16 output is rounded to nearest even.
+ *   lse: NULL or fp32 [B,Hq,Sq].
+ *   Supported: D in {64, 128}; Hq % Hkv == 0; any Sq, Skv >= 0 (0 sizes enqueue nothing
+ *   except, for Skv == 0, the zero output).
+ */
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int dtype, int B, int Sq, int Skv, int Hq, int Hkv, int D, int causal,
+                     float softmax_scale, hipStream_t stream);
+
+/*
+ * Decode (token generation; AMD buffers page, token_gen variant of the K/V buffers):
+ * one query token per sequence attends to keys [0, kv_lens[b]) of its cache.
+ *   q [B,Hq,D] bf16; k_cache, v_cache [B,max_kv_len,Hkv,D] bf16; o [B,Hq,D] bf16;
+ *   kv_lens: DEVICE int32 [B], clamped in-kernel to [0, max_kv_len] (0 gives O = 0).
+ *   lse: NULL or fp32 [B,Hq].
+ * The KV range of every sequence is split across workgroups; each writes a partial
+ * (row max, row sum, unnormalised O) to `workspace`, and a second kernel on the same
+ * stream merges the partials.  workspace: device memory of at least
+ * attn_decode_workspace_size(B, Hq, D, max_kv_len) bytes, owned by the caller.
+ *   Supported: dtype ATTN_BF16, D == 128, Hq % Hkv == 0, Hq / Hkv <= 16.
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int D, int max_kv_len);
+int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
+                    float* lse, const int32_t* kv_lens, int dtype, int B, int Hq, int Hkv,
+                    int D, int max_kv_len, float softmax_scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * MLA prefill with per-token scales (MLASmemStorage page: Q and KV tiles each hold a
+ * nope part in the qkv dtype and a rope part in the rope dtype, plus one fp32 q_scale
+ * per Q row and one k_scale per K row of the tile).  Logits:
+ *   x[i,j] = scale * ( (q_nope_i . k_nope_j) * q_scale_i * k_scale_j + q_rope_i . k_rope_j )
+ *   q_nope [B,Sq,H,Dn], k_nope [B,Skv,H,Dn]: `nope_dtype` (ATTN_FP8_E4M3 or ATTN_BF16);
+ *   q_rope [B,Sq,H,Dr], k_rope [B,Skv,Hr,Dr] (Hr = 1: one rope head shared by all H,
+ *   or Hr = H): bf16; v [B,Skv,H,Dv], o [B,Sq,H,Dv]: bf16;
+ *   q_scale [B,Sq,H], k_scale [B,Skv,H]: fp32, or NULL for all-ones;
+ *   lse: NULL or fp32 [B,H,Sq].
+ *   Supported: (Dn, Dr, Dv) == (128, 64, 128).
+ */
+int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope,
+                    const void* k_rope, const void* v, void* o, const float* q_scale,
+                    const float* k_scale, float* lse, int nope_dtype, int B, int Sq, int Skv,
+                    int H, int Hr, int Dn, int Dr, int Dv, int causal, float softmax_scale,
+                    hipStream_t stream);
+
+/*
+ * MLA decode (KVPipelineGeneric page, MLA decode utilities): H query heads share one
+ * latent KV head; a cache row is [latent Dv | rope Dk-Dv] and serves as K (all Dk
+ * columns) and as V (its first Dv columns), read from HBM once.
+ *   q [B,H,Dk] bf16; kv_cache [B,max_kv_len,Dk] bf16; o [B,H,Dv] bf16;
+ *   kv_lens DEVICE int32 [B] (clamped to [0, max_kv_len]); lse NULL or fp32 [B,H].
+ *   workspace: at least mla_decode_workspace_size(B, H, Dv, max_kv_len) bytes.
+ *   Supported: (Dk, Dv) == (576, 512), H % 16 == 0, H <= 128.
+ */
+size_t mla_decode_workspace_size(int B, int H, int Dv, int max_kv_len);
+int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse,
+                   const int32_t* kv_lens, int B, int H, int Dk, int Dv, int max_kv_len,
+                   float softmax_scale, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: libattn.so loads, exports every function include/attn.h
+declares, and rejects invalid arguments with the documented status before any HIP
+call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_flash_attn_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ESCALE = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+NUL = None
+S = ctypes.c_void_p(0)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.lib()
+
+
+def test_header_declares_the_four_entry_points():
+    names = header_functions()
+    for n in ("attn_prefill_fwd", "attn_decode_fwd", "mla_prefill_fwd", "mla_decode_fwd",
+              "attn_decode_workspace_size", "mla_decode_workspace_size", "attn_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in header_functions():
+        assert hasattr(lib, n), n
+    assert set(header_functions()) == set(fa.EXPORTS)
+
+
+def test_status_strings(lib):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ESCALE):
+        assert fa.status_string(code) and fa.status_string(code) != "unknown status"
+    assert fa.status_string(12345) == "unknown status"
+
+
+def prefill(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=1, B=1, Sq=8, Skv=8, Hq=2, Hkv=1, D=128, causal=0, scale=0.1):
+    return lib.attn_prefill_fwd(q, k, v, o, NUL, dtype, B, Sq, Skv, Hq, Hkv, D, causal, scale, S)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, dtype=2) == EDTYPE
+    assert prefill(lib, dtype=7) == EDTYPE
+    assert prefill(lib, B=-1) == ESHAPE
+    assert prefill(lib, Hq=3, Hkv=2) == ESHAPE
+    assert prefill(lib, Hkv=0) == ESHAPE
+    assert prefill(lib, Sq=-5) == ESHAPE
+    assert prefill(lib, B=1 << 20, Sq=1 << 20, Hq=64, Hkv=64) == ESHAPE   # element count overflow
+    assert prefill(lib, D=96) == EUNSUP
+    assert prefill(lib, D=256) == EUNSUP
+    assert prefill(lib, scale=0.0) == ESCALE
+    assert prefill(lib, scale=float("nan")) == ESCALE
+    assert prefill(lib, scale=float("inf")) == ESCALE
+    assert prefill(lib, q=NUL) == ENULL
+    assert prefill(lib, o=NUL) == ENULL
+    assert prefill(lib, k=NUL) == ENULL
+    # empty problems enqueue nothing and succeed, whatever the pointers
+    assert prefill(lib, q=NUL, k=NUL, v=NUL, o=NUL, B=0) == OK
+    assert prefill(lib, q=NUL, k=NUL, v=NUL, o=NUL, Sq=0) == OK
+
+
+def decode(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, dtype=1, B=4, Hq=32, Hkv=8, D=128, L=1024, scale=0.1,
+           ws=FAKE, wsb=1 << 40):
+    return lib.attn_decode_fwd(q, k, v, o, NUL, lens, dtype, B, Hq, Hkv, D, L, scale, ws, wsb, S)
+
+
+def test_decode_validation(lib):
+    need = lib.attn_decode_workspace_size(4, 32, 128, 1024)
+    assert need > 0
+    assert lib.attn_decode_workspace_size(-1, 32, 128, 1024) == 0
+    assert decode(lib, dtype=0) == EDTYPE
+    assert decode(lib, Hq=30, Hkv=8) == ESHAPE
+    assert decode(lib, L=-1) == ESHAPE
+    assert decode(lib, D=64) == EUNSUP
+    assert decode(lib, Hq=64, Hkv=2) == EUNSUP       # 32 q heads per kv head > 16
+    assert decode(lib, scale=-1.0) == ESCALE
+    assert decode(lib, lens=NUL) == ENULL
+    assert decode(lib, v=NUL) == ENULL
+    assert decode(lib, ws=NUL) == EWS
+    assert decode(lib, wsb=need - 1) == EWS
+    assert decode(lib, B=0, q=NUL, o=NUL, lens=NUL, ws=NUL) == OK
+
+
+def mla_prefill(lib, qn=FAKE, qr=FAKE, kn=FAKE, kr=FAKE, v=FAKE, o=FAKE, dt=2, B=1, Sq=64, Skv=64, H=4, Hr=1,
+                Dn=128, Dr=64, Dv=128, causal=1, scale=0.07):
+    return lib.mla_prefill_fwd(qn, qr, kn, kr, v, o, NUL, NUL, NUL, dt, B, Sq, Skv, H, Hr, Dn, Dr, Dv, causal,
+                               scale, S)
+
+
+def test_mla_prefill_validation(lib):
+    assert mla_prefill(lib, dt=0) == EDTYPE
+    assert mla_prefill(lib, Hr=2) == ESHAPE
+    assert mla_prefill(lib, H=-4) == ESHAPE
+    assert mla_prefill(lib, Dn=64) == EUNSUP
+    assert mla_prefill(lib, Dr=32) == EUNSUP
+    assert mla_prefill(lib, Dv=64) == EUNSUP
+    assert mla_prefill(lib, scale=0.0) == ESCALE
+    assert mla_prefill(lib, qr=NUL) == ENULL
+    assert mla_prefill(lib, kr=NUL) == ENULL
+    assert mla_prefill(lib, B=0, qn=NUL, qr=NUL, kn=NUL, kr=NUL, v=NUL, o=NUL) == OK
+
+
+def mla_decode(lib, q=FAKE, kv=FAKE, o=FAKE, lens=FAKE, B=8, H=128, Dk=576, Dv=512, L=4096, scale=0.04, ws=FAKE,
+               wsb=1 << 40):
+    return lib.mla_decode_fwd(q, kv, o, NUL, lens, B, H, Dk, Dv, L, scale, ws, wsb, S)
+
+
+def test_mla_decode_validation(lib):
+    need = lib.mla_decode_workspace_size(8, 128, 512, 4096)
+    assert need >= 8 * 128 * 514 * 4
+    assert mla_decode(lib, Dv=600) == ESHAPE
+    assert mla_decode(lib, Dk=512) == EUNSUP
+    assert mla_decode(lib, H=100) == EUNSUP
+    assert mla_decode(lib, H=256) == EUNSUP
+    assert mla_decode(lib, scale=float("nan")) == ESCALE
+    assert mla_decode(lib, kv=NUL) == ENULL
+    assert mla_decode(lib, wsb=need - 1) == EWS
+    assert mla_decode(lib, B=0, q=NUL, kv=NUL, o=NUL, lens=NUL, ws=NUL) == OK

@@ -1,0 +1,112 @@
+"""GPU parity of attn_decode_fwd and mla_decode_fwd (split-KV + combine) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import attention_flash_attn_fwd_amd as fa
+import oracle
+from tests.helpers import BF16_TOL, assert_close, assert_lse_close, dev, dev_bf16, host_f64, say
+from workloads import make_decode, make_mla_decode, workload
+
+pytestmark = pytest.mark.gpu
+
+GQA = "gqa_decode_bf16_b64_hq32_hkv8_d128_l8192"
+MLA = "mla_decode_bf16_b64_h128_dk576_dv512_l4096"
+
+
+def _gqa(w, lens=None, batches=None):
+    d = make_decode(w, batches=batches, lens=lens)
+    return dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"]), dev(d["kv_lens"])
+
+
+def _check_gqa(w, lens):
+    say(f"case gqa decode B={w.B} Hq={w.Hq} Hkv={w.Hkv} Lmax={w.Skv} lens={list(lens)[:8]}")
+    q, k, v, kl = _gqa(w, lens=lens)
+    o, lse = fa.decode(q, k, v, kl, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(host_f64(q), host_f64(k), host_f64(v), np.asarray(lens), w.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 1), (12, 4)])
+def test_gqa_decode_small(Hq, Hkv):
+    lens = [1, 31, 32, 33, 257, 1000, 0, 513]
+    w = workload(GQA, B=len(lens), Hq=Hq, Hkv=Hkv, Skv=1000)
+    _check_gqa(w, lens)
+
+
+def test_gqa_decode_long_single_sequence():
+    w = workload(GQA, B=1, Skv=20000)
+    _check_gqa(w, [19999])
+
+
+def test_gqa_decode_full_workload_sampled():
+    """The full decode workload (B64, 32/8 heads, cache 8192, lengths U[1024, 8192]); sampled sequences."""
+    w = workload(GQA)
+    say(f"case {w.name} (sampled sequences)")
+    q, k, v, kl = _gqa(w)
+    o, lse = fa.decode(q, k, v, kl, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    lens = kl.cpu().numpy()
+    picks = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 31]
+    ro, rl = [], []
+    for b in picks:
+        L = int(lens[b])
+        r, l = oracle.decode(host_f64(q[b:b + 1]), host_f64(k[b:b + 1, :L]), host_f64(v[b:b + 1, :L]),
+                             np.array([L]), w.scale)
+        ro.append(r[0]); rl.append(l[0])
+    assert_close(host_f64(o[picks]), np.stack(ro), BF16_TOL, "O sampled")
+    assert_lse_close(lse[picks].cpu().numpy(), np.stack(rl), "LSE sampled")
+
+
+def test_gqa_decode_matches_single_row_prefill():
+    """A decode row equals the last row of a bottom-right causal prefill over the same keys."""
+    w = workload(GQA, B=2, Skv=700)
+    q, k, v, kl = _gqa(w, lens=[700, 700])
+    od = fa.decode(q, k, v, kl, scale=w.scale)
+    op = fa.prefill(q[:, None].contiguous(), k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_close(host_f64(od), host_f64(op[:, 0]), BF16_TOL, "decode vs prefill")
+
+
+def test_gqa_decode_zero_query_gives_mean():
+    lens = [5, 300]
+    w = workload(GQA, B=2, Hq=8, Hkv=2, Skv=300)
+    q, k, v, kl = _gqa(w, lens=lens)
+    q.zero_()
+    o = fa.decode(q, k, v, kl)
+    torch.cuda.synchronize()
+    vv = host_f64(v)
+    ref = np.stack([np.repeat(vv[b, :lens[b]].mean(0), 4, axis=0) for b in range(2)])
+    assert_close(host_f64(o), ref, BF16_TOL, "mean of V")
+
+
+def _mla(w, lens=None):
+    d = make_mla_decode(w, lens=lens)
+    return dev_bf16(d["q"]), dev_bf16(d["kv"]), dev(d["kv_lens"])
+
+
+@pytest.mark.parametrize("H", [128, 16, 64])
+def test_mla_decode_small(H):
+    lens = [1, 33, 300, 0, 128]
+    w = workload(MLA, B=len(lens), Hq=H, Skv=300)
+    say(f"case mla decode H={H} lens={lens}")
+    q, kv, kl = _mla(w, lens=lens)
+    o, lse = fa.mla_decode(q, kv, kl, dv=512, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode(host_f64(q), host_f64(kv), np.asarray(lens), 512, w.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+
+
+def test_mla_decode_full_workload_sampled():
+    w = workload(MLA)
+    say(f"case {w.name} (sampled sequences)")
+    q, kv, kl = _mla(w)
+    o, lse = fa.mla_decode(q, kv, kl, dv=512, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    picks = [0, 37, 63]
+    ro, rl = oracle.mla_decode(host_f64(q[picks]), host_f64(kv[picks]), np.full(3, 4096), 512, w.scale)
+    assert_close(host_f64(o[picks]), ro, BF16_TOL, "O sampled")
+    assert_lse_close(lse[picks].cpu().numpy(), rl, "LSE sampled")

@@ -1,0 +1,115 @@
+"""GPU parity of attn_prefill_fwd (bf16 and fp32) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import attention_flash_attn_fwd_amd as fa
+import oracle
+from tests.helpers import (BF16_TOL, F32_TOL, assert_close, assert_lse_close, dev, dev_bf16, host_f64, say)
+from workloads import make_prefill, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(w):
+    d = make_prefill(w)
+    if w.dtype == "bf16":
+        q, k, v = dev_bf16(d["q"]), dev_bf16(d["k"]), dev_bf16(d["v"])
+    else:
+        q, k, v = dev(d["q"]), dev(d["k"]), dev(d["v"])
+    return q, k, v
+
+
+def _check_full(w, tol):
+    say(f"case {w.name} B={w.B} Sq={w.Sq} Skv={w.Skv} Hq={w.Hq} Hkv={w.Hkv} D={w.D} causal={w.causal}")
+    q, k, v = _inputs(w)
+    o, lse = fa.prefill(q, k, v, causal=w.causal, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill(host_f64(q), host_f64(k), host_f64(v), w.scale, w.causal)
+    assert_close(host_f64(o), ro, tol, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+    return o
+
+
+def test_mha_fp32_workload():
+    _check_full(workload("mha_fp32_b1_h4_s128_d64"), F32_TOL)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_ragged(causal, D):
+    w = workload("mha_fp32_b1_h4_s128_d64", B=2, Sq=150, Skv=150, Hq=4, Hkv=2, D=D, Dv=D, causal=causal,
+                 scale=D ** -0.5)
+    _check_full(w, F32_TOL)
+
+
+BF16_CASES = [
+    # B, Sq, Skv, Hq, Hkv, D, causal
+    (2, 300, 300, 4, 2, 128, False),
+    (2, 300, 300, 4, 2, 128, True),
+    (1, 256, 256, 2, 2, 128, True),     # whole tiles only
+    (1, 77, 333, 4, 4, 128, True),      # Sq < Skv: bottom-right causal
+    (1, 200, 50, 2, 1, 128, True),      # Sq > Skv: leading rows see no key
+    (3, 1, 1000, 4, 1, 128, False),     # one query row
+    (1, 129, 129, 2, 2, 64, False),
+    (1, 129, 129, 4, 1, 64, True),
+    (1, 5, 7, 1, 1, 128, True),         # smaller than one tile
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,D,causal", BF16_CASES)
+def test_bf16_small(B, Sq, Skv, Hq, Hkv, D, causal):
+    w = workload("mha_prefill_causal_bf16_b4_h32_s4096_d128", B=B, Sq=Sq, Skv=Skv, Hq=Hq, Hkv=Hkv, D=D, Dv=D,
+                 causal=causal, scale=D ** -0.5)
+    _check_full(w, BF16_TOL)
+
+
+def test_bf16_empty_kv_gives_zeros():
+    q = torch.randn(1, 16, 2, 128, device="cuda").to(torch.bfloat16)
+    k = torch.empty(1, 0, 2, 128, device="cuda", dtype=torch.bfloat16)
+    o, lse = fa.prefill(q, k, k, causal=False, return_lse=True)
+    torch.cuda.synchronize()
+    assert (o.float() == 0).all() and torch.isneginf(lse).all()
+
+
+def test_bf16_zero_query_gives_prefix_mean():
+    w = workload("mha_prefill_causal_bf16_b4_h32_s4096_d128", B=1, Sq=200, Skv=200, Hq=2, Hkv=2)
+    q, k, v = _inputs(w)
+    q.zero_()
+    o = fa.prefill(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    vv = host_f64(v)
+    pref = np.cumsum(vv, axis=1) / np.arange(1, 201)[None, :, None, None]
+    assert_close(host_f64(o), pref, BF16_TOL, "prefix mean")
+
+
+def test_bf16_deterministic():
+    w = workload("mha_prefill_causal_bf16_b4_h32_s4096_d128", B=1, Sq=333, Skv=333, Hq=4, Hkv=4)
+    q, k, v = _inputs(w)
+    a = fa.prefill(q, k, v, causal=True)
+    b = fa.prefill(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bf16_causal_full_workload_sampled():
+    """The full causal prefill workload (B4 H32 S4096 D128), sampled rows of several heads."""
+    w = workload("mha_prefill_causal_bf16_b4_h32_s4096_d128")
+    say(f"case {w.name} (sampled rows)")
+    q, k, v = _inputs(w)
+    o, lse = fa.prefill(q, k, v, causal=True, scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 2047, 2048, 4094, 4095], rng.integers(0, 4096, 24)]))
+    got, ref, gl, rlse = [], [], [], []
+    for b, h in [(0, 0), (1, 17), (2, 5), (3, 31)]:
+        qs = host_f64(q[b:b + 1, :, h:h + 1])
+        ks = host_f64(k[b:b + 1, :, h:h + 1])
+        vs = host_f64(v[b:b + 1, :, h:h + 1])
+        ro, rl = oracle.prefill_rows(qs, ks, vs, w.scale, True, 0, 0, rows)
+        got.append(host_f64(o[b, rows, h]))
+        ref.append(ro)
+        gl.append(lse[b, h, rows].cpu().numpy())
+        rlse.append(rl)
+    assert_close(np.stack(got), np.stack(ref), BF16_TOL, "O sampled")
+    assert_lse_close(np.stack(gl), np.stack(rlse), "LSE sampled")
