@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the forward-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the path's entry point over the whole workload, inputs resident
+in HBM.  The default workload is the causal bf16 prefill (B4 H32 S4096 D128); the
+others (fp32 MHA, GQA decode, MLA decode, MLA prefill) can be named with --workload.
+Prints one JSON line with the throughput, a roofline object for the dominant kernel
+(algorithmic work per launch / measured launch duration, against MI355X's published
+peak) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
+PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "hbm": 8000.0}   # TFLOP/s, GB/s
+
+
+def algorithmic_work(w, lens=None):
+    """(flops, bytes) of one call: flops over unmasked (query, key) pairs only; bytes = inputs
+    read once + outputs written once (decode: the visible cache rows of each kv head)."""
+    if w.kind == "prefill":
+        if w.causal:
+            off = w.Skv - w.Sq
+            pairs = sum(max(0, min(w.Skv, i + off + 1)) for i in range(w.Sq))
+        else:
+            pairs = w.Sq * w.Skv
+        flops = 2 * (w.D + w.Dv) * pairs * w.B * w.Hq
+        esz = 4 if w.dtype == "f32" else 2
+        byts = esz * w.B * (w.Sq * w.Hq * (w.D + w.Dv) + w.Skv * w.Hkv * (w.D + w.Dv))
+        return flops, byts
+    if w.kind == "decode":
+        sl = int(sum(lens))
+        flops = 2 * w.Hq * (w.D + w.Dv) * sl
+        byts = sl * w.Hkv * (w.D + w.Dv) * 2 + w.B * w.Hq * (w.D + w.Dv) * 2
+        return flops, byts
+    if w.kind == "mla_decode":
+        sl = int(sum(lens))
+        flops = 2 * w.Hq * (w.D + w.Dv) * sl
+        byts = sl * w.D * 2 + w.B * w.Hq * (w.D + w.Dv) * 2
+        return flops, byts
+    if w.kind == "mla_prefill":
+        pairs = w.Sq * (w.Sq + 1) // 2 if w.causal else w.Sq * w.Skv
+        f_fp8 = 2 * w.Dn * pairs * w.B * w.Hq
+        f_bf16 = 2 * (w.Dr + w.Dv) * pairs * w.B * w.Hq
+        byts = w.B * (w.Sq * w.Hq * (w.Dn + 2 * w.Dr + 2 * w.Dv + 4) + w.Skv * w.Hq * (w.Dn + 2 * w.Dv + 4)
+                      + w.Skv * w.Hr * 2 * w.Dr)
+        return (f_fp8, f_bf16), byts
+    raise ValueError(w.kind)
+
+
+# ------------------------------------------------------------------------------- inputs
+
+def setup(w):
+    """Device inputs and the step closure for workload w; returns (step, lens, keepalive)."""
+    import numpy as np
+    import torch
+
+    import attention_flash_attn_fwd_amd as fa
+    from workloads import make_decode, make_mla_decode, make_mla_prefill, make_prefill
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    if w.kind == "prefill":
+        d = make_prefill(w)
+        if w.dtype == "bf16":
+            q, k, v = bf16(d["q"]), bf16(d["k"]), bf16(d["v"])
+        else:
+            q, k, v = (torch.from_numpy(d[n]).cuda() for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        return (lambda i: fa.prefill(q, k, v, causal=w.causal, scale=w.scale, out=o)), None, (q, k, v, o)
+    if w.kind == "decode":
+        d = make_decode(w)
+        q, kv_lens = bf16(d["q"]), torch.from_numpy(d["kv_lens"]).cuda()
+        caches = [(bf16(d["k"]), bf16(d["v"]))]
+        ws = torch.empty(fa.decode_workspace_size(w.B, w.Hq, w.D, w.Skv), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        return (lambda i: fa.decode(q, caches[0][0], caches[0][1], kv_lens, scale=w.scale, workspace=ws, out=o)), \
+            d["kv_lens"], (q, caches, ws, o)
+    if w.kind == "mla_decode":
+        d = make_mla_decode(w)
+        q, kv_lens = bf16(d["q"]), torch.from_numpy(d["kv_lens"]).cuda()
+        # two copies of the 302 MB latent cache, alternated, so the 256 MB MALL cannot serve a step
+        kv0 = bf16(d["kv"])
+        caches = [kv0, kv0.clone()]
+        ws = torch.empty(fa.mla_decode_workspace_size(w.B, w.Hq, w.Dv, w.Skv), dtype=torch.uint8, device="cuda")
+        o = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda")
+        return (lambda i: fa.mla_decode(q, caches[i & 1], kv_lens, dv=w.Dv, scale=w.scale, workspace=ws, out=o)), \
+            d["kv_lens"], (q, caches, ws, o)
+    if w.kind == "mla_prefill":
+        d = make_mla_prefill(w)
+        t = {n: (bf16(d[n]) if d[n].dtype == np.uint16 else torch.from_numpy(d[n]).cuda())
+             for n in ("q_nope", "k_nope", "q_scale", "k_scale", "q_rope", "k_rope", "v")}
+        o = torch.empty((w.B, w.Sq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda")
+        return (lambda i: fa.mla_prefill(t["q_nope"], t["q_rope"], t["k_nope"], t["k_rope"], t["v"], t["q_scale"],
+                                         t["k_scale"], causal=w.causal, scale=w.scale, out=o)), None, (t, o)
+    raise ValueError(w.kind)
+
+
+# ------------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(w, lens, budget_s: float):
+    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    from workloads import make_decode, make_mla_decode, make_mla_prefill, make_prefill
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+
+    done_work, t_used, n, what = 0.0, 0.0, 0, ""
+    if w.kind in ("prefill", "mla_prefill"):
+        pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+        cache = {}
+        for b, h in pairs:
+            if b not in cache:
+                cache = {b: (make_prefill(w, batches=[b]) if w.kind == "prefill" else make_mla_prefill(w, batches=[b]))}
+            d = cache[b]
+            t0 = time.perf_counter()
+            for r0 in range(0, w.Sq, 1024):
+                rows = np.arange(r0, min(w.Sq, r0 + 1024))
+                if w.kind == "prefill":
+                    kvh = h // (w.Hq // w.Hkv)
+                    dec = oracle.bf16_to_f64 if w.dtype == "bf16" else (lambda x: x.astype(np.float64))
+                    oracle.prefill_rows(dec(d["q"][:, :, h:h + 1]), dec(d["k"][:, :, kvh:kvh + 1]),
+                                        dec(d["v"][:, :, kvh:kvh + 1]), w.scale, w.causal, 0, 0, rows)
+                else:
+                    s = lambda a: a[:, :, h:h + 1]
+                    oracle.mla_prefill_rows(oracle.e4m3_to_f64(s(d["q_nope"])), oracle.bf16_to_f64(s(d["q_rope"])),
+                                            oracle.e4m3_to_f64(s(d["k_nope"])), oracle.bf16_to_f64(d["k_rope"]),
+                                            oracle.bf16_to_f64(s(d["v"])), s(d["q_scale"]).astype(np.float64),
+                                            s(d["k_scale"]).astype(np.float64), w.scale, w.causal, 0, 0, rows)
+            t_used += time.perf_counter() - t0
+            n += 1
+            if t_used >= budget_s:
+                break
+        one = w.with_(B=1, Hq=1, Hkv=1)
+        f, _ = algorithmic_work(one)
+        done_work = (sum(f) if isinstance(f, tuple) else f) * n
+        what = f"{n} (batch, head) pairs x all {w.Sq} query rows"
+        return {"value": done_work / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": what, "seconds": round(t_used, 2)}
+    # decode: whole sequences
+    sel = []
+    for b in range(w.B):
+        t0 = time.perf_counter()
+        if w.kind == "decode":
+            d = make_decode(w, batches=[b], lens=lens)
+            L = int(d["kv_lens"][0])
+            oracle.decode(oracle.bf16_to_f64(d["q"]), oracle.bf16_to_f64(d["k"][:, :L]),
+                          oracle.bf16_to_f64(d["v"][:, :L]), d["kv_lens"], w.scale)
+        else:
+            d = make_mla_decode(w, batches=[b], lens=lens)
+            L = int(d["kv_lens"][0])
+            oracle.mla_decode(oracle.bf16_to_f64(d["q"]), oracle.bf16_to_f64(d["kv"][:, :L]), d["kv_lens"], w.Dv,
+                              w.scale)
+        t_used += time.perf_counter() - t0
+        sel.append(L)
+        if t_used >= budget_s:
+            break
+    _, byts = algorithmic_work(w.with_(B=len(sel)), lens=sel)
+    return {"value": byts / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(sel)} whole sequences (lengths {sel[:4]}...)", "seconds": round(t_used, 2)}
+
+
+# ------------------------------------------------------------------------------- main
+
+def main():
+    from workloads.shapes import BENCH_DEFAULT, WORKLOADS
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=BENCH_DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU sample")
+    ap.add_argument("--traffic", default=None, help="JSON file with HBM traffic per launch from rocprofv3 counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is a design note, "
+              "not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import workload
+    w = workload(args.workload)
+    torch.cuda.set_device(0)
+    step, lens, keep = setup(w)
+    flops, byts = algorithmic_work(w, lens)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+
+    if w.kind in ("prefill", "mla_prefill"):
+        if w.kind == "mla_prefill":
+            f_fp8, f_bf16 = flops
+            total = f_fp8 + f_bf16
+            t_roof = f_fp8 / (PEAK["fp8"] * 1e12) + f_bf16 / (PEAK["bf16"] * 1e12)
+            peak = total / t_roof / 1e12          # mixed-precision peak: frac = T_roof / T_measured
+        else:
+            total = flops
+            peak = PEAK["f32" if w.dtype == "f32" else "bf16"]
+        value = total / (ms_per_step * 1e-3) / 1e12
+        achieved = total / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+        unit = "TFLOP/s"
+    else:
+        value = byts / (ms_per_step * 1e-3) / 1e9
+        achieved = byts / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm"], "unit": "GB/s",
+                "frac": round(achieved / PEAK["hbm"], 4)}
+        unit = "GB/s"
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
+    roof["traffic"] = traffic
+
+    cfg = {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+           "Dv": w.Dv, "causal": w.causal, "parallelism": "none (1 GPU)"}
+    if w.kind == "mla_prefill":
+        cfg.update({"Dn": w.Dn, "Dr": w.Dr, "Hr": w.Hr})
+    if lens is not None:
+        cfg.update({"sum_kv_len": int(sum(lens)), "len_range": [w.len_lo, w.len_hi]})
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16"}[w.dtype],
+        "data": "synthetic (seeded N(0,1), see workloads/)", "config": cfg, "roofline": roof,
+        "kernel_ms": round(launch_ms, 4), "algorithmic": {"flops": flops if not isinstance(flops, tuple) else list(flops),
+                                                          "bytes": byts},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
