@@ -83,6 +83,19 @@ __device__ __forceinline__ void dma4(const void* g, FA_LDS char* lds) {
   __builtin_amdgcn_global_load_lds(g, (FA_LDS void*)lds, 4, 0, 0);
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0) for the
+// buffer_load ... lds form of the direct copy: the source address is an SGPR base plus a
+// per-lane 32-bit offset, so no per-lane 64-bit address arithmetic is needed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, FA_LDS char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t r, FA_LDS char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds, 4, voff, 0, 0, 0);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 template <int N>
@@ -151,6 +164,12 @@ __device__ __forceinline__ float xor16_sum(float x) {
 // ------------------------------------------------------------------ numerics
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// acc + a.lo * b.lo + a.hi * b.hi over packed bf16 pairs (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(int a, int b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+constexpr int kBf16PairOne = 0x3F803F80;  // packed bf16 {1.0, 1.0}
 
 // two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ int pack_bf16(float a, float b) {

@@ -1,15 +1,21 @@
-// Prefill forward kernels (MHA / GQA in bf16 or fp32, and MLA with e4m3 nope + bf16 rope).
+// Prefill forward kernels on bf16 matrix cores: MHA / GQA (bf16 q/k/v) and MLA with
+// per-token scales (e4m3 or bf16 nope part, bf16 rope part, bf16 V).
 //
 // Method: the flash-attention forward that Modular's "KVPipelineGeneric" page describes
-// (S = Q.K' and O += P.V per K/V tile, over a pipeline of K/V stages), with the online
+// (S = Q.K' and O += P.V per K/V tile over a pipeline of K/V stages), with the online
 // softmax whose per-row correction the "MLASmemStorage" page keeps in a correction
-// buffer: here the correction factor stays in the lane that owns the row.  The AMD
-// "buffers" page's roles map as follows: QRegisterBuffer -> Q fragments in VGPRs;
-// KBufferLDS / KVBufferLDS (direct DRAM->LDS, no register staging) -> global_load_lds
-// into a swizzled two-stage LDS ring; VBufferTransposeLoads -> ds_read_b64_tr_b16;
-// PRegisterBuffer -> P packed to bf16 in VGPRs; OutputRegisterBuffer -> O^T accumulators.
+// buffer; here the correction stays in the lane that owns the row.  The AMD "buffers"
+// page's roles map as follows: QRegisterBuffer -> Q fragments in VGPRs for the whole
+// block; KBufferLDS / KVBufferLDS (direct DRAM->LDS, no register staging) ->
+// buffer_load ... lds into a swizzled two-stage LDS ring; VBufferTransposeLoads ->
+// ds_read_b64_tr_b16; PRegisterBuffer -> P packed to bf16 in VGPRs straight from the S^T
+// accumulators; OutputRegisterBuffer -> O^T accumulators.
 //
-// Workgroup: 4 waves, BM = 128 query rows (32 per wave), K/V tiles of BN = 64 keys.
+// Workgroup: 4 waves, query blocks of BM = 128 rows (32 per wave), K/V tiles of BN = 64
+// keys.  Causal workgroups take a pair of query blocks (i, n-1-i), so every workgroup has
+// the same number of key tiles; workgroups are ordered head-major within each XCD (the
+// dispatcher deals workgroups to the 8 XCDs round-robin), so the workgroups of one
+// (batch, head) run together and share its K/V through that XCD's L2.
 #include "device.h"
 #include "launch.h"
 
@@ -19,10 +25,57 @@ namespace {
 constexpr int BM = 128;
 constexpr int BN = 64;
 constexpr int NW = 4;
+// Lazy rescaling: the running reference max only moves when a row max exceeds it by more
+// than 8 (log2 units), so P values stay <= 2^8; O and l share the reference, so O / l is
+// unchanged and most tiles skip the rescale.
+constexpr float kRescaleLog2 = 8.f;
+
+template <int ROWB>
+__device__ __forceinline__ uint32_t swz_rows(uint32_t row) {
+  static_assert(ROWB == 256 || ROWB == 128, "row size");
+  return ROWB == 256 ? swz256(row) : swz_half(row);
+}
+
+// A tile of BN rows of ROWB bytes copied global -> LDS by the NW waves with 16-byte direct
+// loads.  LDS row r holds tile row r with its chunks XOR-permuted by swz_rows(r): each lane
+// fetches the global chunk that belongs at its LDS slot.  Per-lane source offsets are
+// computed once; a tile costs one instruction per wave per KiB.
+template <int ROWB>
+struct RowDma {
+  static constexpr int RPI = 1024 / ROWB;           // rows per wave instruction
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
+  static constexpr int NI = BN * ROWB / 1024 / NW;  // instructions per wave per tile
+  static_assert(NI >= 1, "tile too small");
+  uint32_t voff[NI];
+
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t stride) {
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+      const uint32_t row = (i * NW + wave) * RPI + lane / CPR;
+      voff[i] = row * stride + ((((uint32_t)lane % CPR) ^ swz_rows<ROWB>(row)) << 4);
+    }
+  }
+  // Rows [0, valid) of the tile start at `base`, `stride` bytes apart; LDS rows at or past
+  // `valid` receive a copy of row valid - 1 (never read as keys: they are masked).
+  __device__ __forceinline__ void issue(const char* base, uint32_t stride, int valid, FA_LDS char* dst, int wave,
+                                        int lane) const {
+    const auto r = make_rsrc(base, (uint32_t)(valid - 1) * stride + ROWB);
+    if (valid >= BN) {
+#pragma unroll
+      for (int i = 0; i < NI; i++) dma16_buf(r, dst + (i * NW + wave) * 1024, voff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; i++) {
+        const uint32_t row = (i * NW + wave) * RPI + lane / CPR;
+        const uint32_t rc = min(row, (uint32_t)(valid - 1));
+        dma16_buf(r, dst + (i * NW + wave) * 1024, rc * stride + ((((uint32_t)lane % CPR) ^ swz_rows<ROWB>(row)) << 4));
+      }
+    }
+  }
+};
 
 // ------------------------------------------------------------------------------------
-// Q.K^T policies: how Q is held in registers, how the K part of a tile is laid out in
-// LDS, and how one 32-key block of S^T is formed.
+// Q.K^T policies: Q in registers, the K part of an LDS stage, one 32-key block of S^T.
 
 // MHA / GQA: bf16 q/k of head dim D.
 template <int D>
@@ -32,45 +85,41 @@ struct QkBf16 {
   struct QFrag {
     i32x4_t c[D / 16];
   };
-  __device__ static uint32_t swz(uint32_t row) { return D == 128 ? swz256(row) : swz_half(row); }
+  struct Lane {
+    RowDma<ROWB> dma;
+    uint32_t ka[D / 16];  // LDS offset of this lane's K chunk for MFMA step c (block 0)
+  };
 
+  __device__ static void init(const PrefillArgs& p, int wave, int lane, Lane& s) {
+    s.dma.init(wave, lane, p.Hkv * ROWB);
+    const uint32_t l32 = lane & 31, hl = lane >> 5, sw = swz_rows<ROWB>(l32);
+#pragma unroll
+    for (int c = 0; c < D / 16; c++) s.ka[c] = l32 * ROWB + (((2 * c + hl) ^ sw) << 4);
+  }
   __device__ static void load_q(const PrefillArgs& p, int b, int h, int qrow, int hl, QFrag& q) {
     const char* base = (const char*)p.q + (((size_t)b * p.Sq + qrow) * p.Hq + h) * (size_t)ROWB;
 #pragma unroll
     for (int c = 0; c < D / 16; c++) q.c[c] = *(const i32x4_t*)(base + c * 32 + hl * 16);
   }
-
-  __device__ static void load_k(const PrefillArgs& p, int b, int h, int kvh, int key0, FA_LDS char* dst,
-                                int wave, int lane) {
-    constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16, NI = KBYTES / 1024 / NW;
-#pragma unroll
-    for (int i = 0; i < NI; i++) {
-      int blk = i * NW + wave;
-      int row = blk * RPI + lane / CPR;
-      int lch = (lane % CPR) ^ swz(row);
-      int key = min(key0 + row, p.Skv - 1);
-      const char* g = (const char*)p.k + (((size_t)b * p.Skv + key) * p.Hkv + kvh) * (size_t)ROWB + lch * 16;
-      dma16(g, dst + blk * 1024);
-    }
+  __device__ static void issue(const PrefillArgs& p, const Lane& s, int b, int h, int kvh, int key0, FA_LDS char* dst,
+                               int wave, int lane) {
+    (void)h;
+    const char* base = (const char*)p.k + (((size_t)b * p.Skv + key0) * p.Hkv + kvh) * (size_t)ROWB;
+    s.dma.issue(base, p.Hkv * ROWB, min(BN, p.Skv - key0), dst, wave, lane);
   }
-
-  __device__ static void scores(const QFrag& q, const FA_LDS char* kt, int kb, int l32, int hl, f32x16_t& s,
-                                bool /*has_kscale*/) {
-    const int row = 32 * kb + l32;
-    const FA_LDS char* r = kt + row * ROWB;
-    const uint32_t sw = swz(row);
-    s = f32x16_t{};
+  template <int OFF>
+  __device__ static void scores(const QFrag& q, const Lane& s, const FA_LDS char* smem, int kb, int hl,
+                                f32x16_t& acc, bool /*has_kscale*/) {
+    (void)hl;
+    acc = f32x16_t{};
 #pragma unroll
-    for (int c = 0; c < D / 16; c++) {
-      i32x4_t a = lds_b128(r + (((2 * c + hl) ^ sw) << 4));
-      s = mfma32x32x16_bf16(a, q.c[c], s);
-    }
+    for (int c = 0; c < D / 16; c++) acc = mfma32x32x16_bf16(lds_b128(smem + s.ka[c] + (OFF + kb * 32 * ROWB)), q.c[c], acc);
   }
 };
 
-// MLA prefill with per-token scales: nope part (Dn = 128) in e4m3 or bf16, rope part
-// (Dr = 64) in bf16 with Hr rope heads, fp32 q_scale per query row and k_scale per key.
-// K part of a stage: k_nope [BN][Dn] | k_rope [BN][64] bf16 (128-byte rows) | k_scale [BN] fp32.
+// MLA prefill with per-token scales: nope (Dn = 128) in e4m3 or bf16, rope (Dr = 64) bf16
+// with Hr rope heads, fp32 q_scale per query row and k_scale per key.
+// K part of a stage: k_nope [BN][Dn] | k_rope [BN][64] bf16 | k_scale [BN] fp32.
 template <bool FP8>
 struct QkMla {
   static constexpr int NROWB = FP8 ? 128 : 256;
@@ -78,22 +127,49 @@ struct QkMla {
   static constexpr int KR = BN * NROWB;
   static constexpr int KS = KR + BN * 128;
   static constexpr int KBYTES = KS + BN * 4;
+  static constexpr int NNA = FP8 ? 4 : 8;
   struct QFrag {
-    i32x8_t n8[2];        // e4m3: 2 x (32 bytes) per lane
+    i32x8_t n8[FP8 ? 2 : 1];  // e4m3: 2 MFMA steps of 32 bytes per lane
     i32x4_t n16[FP8 ? 1 : 8];
     i32x4_t r[4];
     float qs;
   };
-  __device__ static uint32_t nswz(uint32_t row) { return FP8 ? swz_half(row) : swz256(row); }
+  struct Lane {
+    RowDma<NROWB> ndma;
+    RowDma<128> rdma;
+    uint32_t na[NNA];  // nope chunk offsets
+    uint32_t ra[4];    // rope chunk offsets
+    uint32_t sa;       // k_scale offset of this lane's first key
+  };
 
+  __device__ static void init(const PrefillArgs& p, int wave, int lane, Lane& s) {
+    s.ndma.init(wave, lane, p.Hq * NROWB);
+    s.rdma.init(wave, lane, p.Hr * 128);
+    const uint32_t l32 = lane & 31, hl = lane >> 5;
+    if constexpr (FP8) {
+      const uint32_t sw = swz_half(l32);
+#pragma unroll
+      for (int c = 0; c < 2; c++)
+#pragma unroll
+        for (int e = 0; e < 2; e++) s.na[2 * c + e] = KN + l32 * 128 + (((4 * c + 2 * hl + e) ^ sw) << 4);
+    } else {
+      const uint32_t sw = swz256(l32);
+#pragma unroll
+      for (int c = 0; c < 8; c++) s.na[c] = KN + l32 * 256 + (((2 * c + hl) ^ sw) << 4);
+    }
+    const uint32_t swr = swz_half(l32);
+#pragma unroll
+    for (int c = 0; c < 4; c++) s.ra[c] = KR + l32 * 128 + (((2 * c + hl) ^ swr) << 4);
+    s.sa = KS + 16 * hl;
+  }
   __device__ static void load_q(const PrefillArgs& p, int b, int h, int qrow, int hl, QFrag& q) {
     const size_t tok = ((size_t)b * p.Sq + qrow) * p.Hq + h;
     const char* n = (const char*)p.q + tok * NROWB;
     if constexpr (FP8) {
 #pragma unroll
       for (int c = 0; c < 2; c++) {
-        i32x4_t lo = *(const i32x4_t*)(n + c * 64 + hl * 32);
-        i32x4_t hi = *(const i32x4_t*)(n + c * 64 + hl * 32 + 16);
+        const i32x4_t lo = *(const i32x4_t*)(n + c * 64 + hl * 32);
+        const i32x4_t hi = *(const i32x4_t*)(n + c * 64 + hl * 32 + 16);
         q.n8[c] = i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
     } else {
@@ -105,94 +181,123 @@ struct QkMla {
     for (int c = 0; c < 4; c++) q.r[c] = *(const i32x4_t*)(r + c * 32 + hl * 16);
     q.qs = p.q_scale ? p.q_scale[tok] : 1.f;
   }
-
-  __device__ static void load_k(const PrefillArgs& p, int b, int h, int kvh, int key0, FA_LDS char* dst,
-                                int wave, int lane) {
+  __device__ static void issue(const PrefillArgs& p, const Lane& s, int b, int h, int kvh, int key0, FA_LDS char* dst,
+                               int wave, int lane) {
     (void)kvh;
-    {  // nope
-      constexpr int RPI = 1024 / NROWB, CPR = NROWB / 16, NI = BN * NROWB / 1024 / NW;
-#pragma unroll
-      for (int i = 0; i < NI; i++) {
-        int blk = i * NW + wave;
-        int row = blk * RPI + lane / CPR;
-        int lch = (lane % CPR) ^ nswz(row);
-        int key = min(key0 + row, p.Skv - 1);
-        const char* g = (const char*)p.k + (((size_t)b * p.Skv + key) * p.Hq + h) * (size_t)NROWB + lch * 16;
-        dma16(g, dst + KN + blk * 1024);
-      }
-    }
-    {  // rope: 128-byte rows, 8 per wave instruction
-      const int hr = p.Hr == 1 ? 0 : h;
-#pragma unroll
-      for (int i = 0; i < BN * 128 / 1024 / NW; i++) {
-        int blk = i * NW + wave;
-        int row = blk * 8 + lane / 8;
-        int lch = (lane % 8) ^ swz_half(row);
-        int key = min(key0 + row, p.Skv - 1);
-        const char* g = (const char*)p.k_rope + (((size_t)b * p.Skv + key) * p.Hr + hr) * 128 + lch * 16;
-        dma16(g, dst + KR + blk * 1024);
-      }
-    }
+    const int valid = min(BN, p.Skv - key0);
+    s.ndma.issue((const char*)p.k + (((size_t)b * p.Skv + key0) * p.Hq + h) * (size_t)NROWB, p.Hq * NROWB, valid,
+                 dst + KN, wave, lane);
+    const int hr = p.Hr == 1 ? 0 : h;
+    s.rdma.issue((const char*)p.k_rope + (((size_t)b * p.Skv + key0) * p.Hr + hr) * 128, p.Hr * 128, valid, dst + KR,
+                 wave, lane);
     if (p.k_scale && wave == 0) {
-      int key = min(key0 + lane, p.Skv - 1);
-      dma4(p.k_scale + ((size_t)b * p.Skv + key) * p.Hq + h, dst + KS);
+      const float* base = p.k_scale + ((size_t)b * p.Skv + key0) * p.Hq + h;
+      const auto r = make_rsrc(base, (uint32_t)((valid - 1) * p.Hq + 1) * 4);
+      dma4_buf(r, dst + KS, (uint32_t)min(lane, valid - 1) * p.Hq * 4);
     }
   }
-
-  __device__ static void scores(const QFrag& q, const FA_LDS char* kt, int kb, int l32, int hl, f32x16_t& s,
-                                bool has_kscale) {
-    const int row = 32 * kb + l32;
+  template <int OFF>
+  __device__ static void scores(const QFrag& q, const Lane& s, const FA_LDS char* smem, int kb, int hl,
+                                f32x16_t& acc, bool has_kscale) {
+    (void)hl;
     f32x16_t sn{};
-    {
-      const FA_LDS char* r = kt + KN + row * NROWB;
-      const uint32_t sw = nswz(row);
-      if constexpr (FP8) {
+    if constexpr (FP8) {
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-          i32x4_t lo = lds_b128(r + (((4 * c + 2 * hl) ^ sw) << 4));
-          i32x4_t hi = lds_b128(r + (((4 * c + 2 * hl + 1) ^ sw) << 4));
-          sn = mfma32x32x64_e4m3(i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, q.n8[c], sn);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; c++) sn = mfma32x32x16_bf16(lds_b128(r + (((2 * c + hl) ^ sw) << 4)), q.n16[c], sn);
+      for (int c = 0; c < 2; c++) {
+        const i32x4_t lo = lds_b128(smem + s.na[2 * c] + (OFF + kb * 32 * NROWB));
+        const i32x4_t hi = lds_b128(smem + s.na[2 * c + 1] + (OFF + kb * 32 * NROWB));
+        sn = mfma32x32x64_e4m3(i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, q.n8[c], sn);
       }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; c++) sn = mfma32x32x16_bf16(lds_b128(smem + s.na[c] + (OFF + kb * 32 * NROWB)), q.n16[c], sn);
     }
     f32x16_t sr{};
-    {
-      const FA_LDS char* r = kt + KR + row * 128;
-      const uint32_t sw = swz_half(row);
 #pragma unroll
-      for (int c = 0; c < 4; c++) sr = mfma32x32x16_bf16(lds_b128(r + (((2 * c + hl) ^ sw) << 4)), q.r[c], sr);
-    }
-    // lane holds keys 32kb + 8j + 4hl + i for register 4j + i
+    for (int c = 0; c < 4; c++) sr = mfma32x32x16_bf16(lds_b128(smem + s.ra[c] + (OFF + kb * 32 * 128)), q.r[c], sr);
+    // this lane holds keys 32kb + 8j + 4hl + i in register 4j + i
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      f32x4_t ks = has_kscale ? lds_f32x4(kt + KS + (32 * kb + 8 * j + 4 * hl) * 4) : f32x4_t{1.f, 1.f, 1.f, 1.f};
+      const f32x4_t ks = has_kscale ? lds_f32x4(smem + s.sa + (OFF + (32 * kb + 8 * j) * 4)) : f32x4_t{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int i = 0; i < 4; i++) s[4 * j + i] = fmaf(sn[4 * j + i], q.qs * ks[i], sr[4 * j + i]);
+      for (int i = 0; i < 4; i++) acc[4 * j + i] = fmaf(sn[4 * j + i], q.qs * ks[i], sr[4 * j + i]);
     }
   }
 };
 
-// V tile [BN][DV] bf16 of kv head `kvh`, rows swizzled like K.
+// ------------------------------------------------------------------------------------
+// Per-row running state and the per-tile step.
+
 template <int DV>
-__device__ __forceinline__ void load_v(const PrefillArgs& p, int b, int kvh, int key0, FA_LDS char* dst, int wave,
-                                       int lane) {
-  constexpr int ROWB = DV * 2, RPI = 1024 / ROWB, CPR = ROWB / 16, NI = BN * ROWB / 1024 / NW;
+struct RowAcc {
+  f32x16_t o[DV / 32];  // O^T: register v of block db holds d = 32db + 8(v/4) + 4hl + v%4
+  float m_ref;          // reference max of the raw scores (-inf before the first visible key)
+  float neg;            // -max(m_ref, 0 if -inf) * c
+  float l;              // lane-partial sum of the bf16-rounded P of this lane's keys
+};
+
+template <class QK, int DV, bool CAUSAL, int OFF, int KPART>
+__device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFrag& q, const typename QK::Lane& ks,
+                                          const uint32_t (&va)[2][DV / 32], const FA_LDS char* smem, int key0,
+                                          bool masked, int qrow, int off, int Skv, float c, int hl, bool has_ks) {
+  constexpr int VROWB = DV * 2;
+  f32x16_t s[BN / 32];
 #pragma unroll
-  for (int i = 0; i < NI; i++) {
-    int blk = i * NW + wave;
-    int row = blk * RPI + lane / CPR;
-    int lch = (lane % CPR) ^ (DV == 128 ? swz256(row) : swz_half(row));
-    int key = min(key0 + row, p.Skv - 1);
-    const char* g = (const char*)p.v + (((size_t)b * p.Skv + key) * p.Hkv + kvh) * (size_t)ROWB + lch * 16;
-    dma16(g, dst + blk * 1024);
+  for (int kb = 0; kb < BN / 32; kb++) QK::template scores<OFF>(q, ks, smem, kb, hl, s[kb], has_ks);
+  if (masked) {
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * hl + (v & 3);
+        const bool vis = key < Skv && (!CAUSAL || key <= qrow + off);
+        s[kb][v] = vis ? s[kb][v] : -INFINITY;
+      }
   }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kb][v]);
+  mx = xor32_max(mx);
+  if (__builtin_amdgcn_ballot_w64(mx * c > st.m_ref * c + kRescaleLog2)) {
+    const float m_new = fmaxf(st.m_ref, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2_fast((st.m_ref - m_use) * c);
+    st.l *= alpha;
+#pragma unroll
+    for (int d = 0; d < DV / 32; d++) st.o[d] *= alpha;
+    st.m_ref = m_new;
+    st.neg = -m_use * c;
+  }
+  i32x4_t pb[BN / 32][2];
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+    for (int tp = 0; tp < 2; tp++) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) e[i] = exp2_fast(fmaf(s[kb][8 * tp + i], c, st.neg));
+      pb[kb][tp] = i32x4_t{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
+#pragma unroll
+      for (int i = 0; i < 4; i++) st.l = dot2_bf16(pb[kb][tp][i], kBf16PairOne, st.l);
+    }
+  // O^T += V^T . P^T
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+    for (int tp = 0; tp < 2; tp++)
+#pragma unroll
+      for (int db = 0; db < DV / 32; db++) {
+        constexpr int base = OFF + KPART;
+        const int rows = (32 * kb + 16 * tp) * VROWB;
+        const i32x2_t lo = lds_tr16(smem + va[0][db] + (base + rows));
+        const i32x2_t hi = lds_tr16(smem + va[1][db] + (base + rows));
+        st.o[db] = mfma32x32x16_bf16(cat(lo, hi), pb[kb][tp], st.o[db]);
+      }
 }
 
 // ------------------------------------------------------------------------------------
-// The bf16 / MLA prefill kernel.
 
 template <class QK, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qblocks) {
@@ -205,238 +310,120 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qb
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hl = lane >> 5;
 
-  // work item: q-blocks with the most keys first when causal
-  const int BH = p.B * p.Hq;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x % BH;
-  const int qb = CAUSAL ? (n_qblocks - 1 - rank) : rank;
+  // work item: contiguous per XCD (workgroup i runs on XCD i % 8), head-major
+  const int G = gridDim.x, x = blockIdx.x % 8, jx = blockIdx.x / 8;
+  const int w = x * (G / 8) + min(x, G % 8) + jx;
+  const int per_head = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;
+  const int bh = w / per_head, it = w % per_head;
   const int b = bh / p.Hq, h = bh % p.Hq;
   const int kvh = h / (p.Hq / p.Hkv);
-  const int q0 = qb * BM;
-  const int off = p.Skv - p.Sq;
-
-  int kv_end = p.Skv;
-  if (CAUSAL) kv_end = max(0, min(p.Skv, min(q0 + BM, p.Sq) - 1 + off + 1));
-  const int n_tiles = (kv_end + BN - 1) / BN;
-
-  const int wrow0 = q0 + 32 * wave;                      // first query row of this wave
-  int wave_end = kv_end, mask_from = p.Skv / BN;
+  int blk[2] = {it, it};
+  int nblk = 1;
   if (CAUSAL) {
-    wave_end = max(0, min(kv_end, wrow0 + 31 + off + 1));
-    const int lim = wrow0 + off + 1;
-    mask_from = min(mask_from, lim > 0 ? lim / BN : 0);
+    blk[0] = n_qblocks - 1 - it;
+    blk[1] = it;
+    nblk = blk[0] == blk[1] ? 1 : 2;
   }
-  const int wave_tiles = (wave_end + BN - 1) / BN;
 
-  const int qrow = wrow0 + l32;
-  const int qrow_c = min(qrow, p.Sq - 1);
+  typename QK::Lane kl;
+  QK::init(p, wave, lane, kl);
+  RowDma<VROWB> vdma;
+  vdma.init(wave, lane, p.Hkv * VROWB);
+  uint32_t va[2][DV / 32];
+  {
+    const uint32_t g = lane >> 4, i16 = lane & 15;
+    const uint32_t row0 = 4 * (g >> 1) + (i16 >> 2), col0 = 16 * (g & 1) + 4 * (i16 & 3);
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int db = 0; db < DV / 32; db++) {
+        const uint32_t row = row0 + 8 * u, col = col0 + 32 * db;
+        va[u][db] = row * VROWB + ((((col >> 3)) ^ swz_rows<VROWB>(row)) << 4) + (((col >> 2) & 1) << 3);
+      }
+  }
   const float c = p.scale * kLog2e;
+  const int off = p.Skv - p.Sq;
   const bool has_ks = p.k_scale != nullptr;
 
-  typename QK::QFrag qf;
-  QK::load_q(p, b, h, qrow_c, hl, qf);
+  auto issue = [&](int t, FA_LDS char* dst) {
+    const int key0 = t * BN;
+    QK::issue(p, kl, b, h, kvh, key0, dst, wave, lane);
+    vdma.issue((const char*)p.v + (((size_t)b * p.Skv + key0) * p.Hkv + kvh) * (size_t)VROWB, p.Hkv * VROWB,
+               min(BN, p.Skv - key0), dst + KPART, wave, lane);
+  };
 
-  RowState st{-INFINITY, 0.f};
-  f32x16_t o[DV / 32];
-#pragma unroll
-  for (int d = 0; d < DV / 32; d++) o[d] = f32x16_t{};
-
-  if (n_tiles > 0) {
-    QK::load_k(p, b, h, kvh, 0, smem, wave, lane);
-    load_v<DV>(p, b, kvh, 0, smem + KPART, wave, lane);
-  }
-
-  const int g = lane >> 4, i16 = lane & 15;
-  for (int t = 0; t < n_tiles; t++) {
-    FA_LDS char* cur = smem + (t & 1) * STAGE;
-    wait_vmcnt<0>();
-    barrier();
-    if (t + 1 < n_tiles) {
-      FA_LDS char* nxt = smem + ((t + 1) & 1) * STAGE;
-      QK::load_k(p, b, h, kvh, (t + 1) * BN, nxt, wave, lane);
-      load_v<DV>(p, b, kvh, (t + 1) * BN, nxt + KPART, wave, lane);
+  for (int bi = 0; bi < nblk; bi++) {
+    const int q0 = blk[bi] * BM;
+    int kv_end = p.Skv;
+    if (CAUSAL) kv_end = max(0, min(p.Skv, min(q0 + BM, p.Sq) - 1 + off + 1));
+    const int n_tiles = (kv_end + BN - 1) / BN;
+    const int wrow0 = q0 + 32 * wave;
+    int wave_end = kv_end, mask_from = p.Skv / BN;
+    if (CAUSAL) {
+      wave_end = max(0, min(kv_end, wrow0 + 31 + off + 1));
+      const int lim = wrow0 + off + 1;
+      mask_from = min(mask_from, lim > 0 ? lim / BN : 0);
     }
-    if (t >= wave_tiles) continue;
+    const int wave_tiles = (wave_end + BN - 1) / BN;
+    const int qrow = wrow0 + l32;
 
-    f32x16_t s[BN / 32];
+    typename QK::QFrag qf;
+    QK::load_q(p, b, h, min(qrow, p.Sq - 1), hl, qf);
+    RowAcc<DV> st;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++) QK::scores(qf, cur, kb, l32, hl, s[kb], has_ks);
+    for (int d = 0; d < DV / 32; d++) st.o[d] = f32x16_t{};
+    st.m_ref = -INFINITY;
+    st.neg = 0.f;
+    st.l = 0.f;
 
-    if (t >= mask_from) {
-#pragma unroll
-      for (int kb = 0; kb < BN / 32; kb++)
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-          const int key = t * BN + 32 * kb + 8 * (v >> 2) + 4 * hl + (v & 3);
-          const bool vis = key < p.Skv && (!CAUSAL || key <= qrow + off);
-          s[kb][v] = vis ? s[kb][v] : -INFINITY;
-        }
+    if (bi > 0) barrier();  // every wave is done reading the previous block's last stage
+    if (n_tiles > 0) issue(0, smem);
+    for (int t = 0; t < n_tiles; t += 2) {
+      wait_vmcnt<0>();
+      barrier();
+      if (t + 1 < n_tiles) issue(t + 1, smem + STAGE);
+      if (t < wave_tiles)
+        tile_step<QK, DV, CAUSAL, 0, KPART>(st, qf, kl, va, smem, t * BN, t >= mask_from, qrow, off, p.Skv, c, hl, has_ks);
+      if (t + 1 >= n_tiles) break;
+      wait_vmcnt<0>();
+      barrier();
+      if (t + 2 < n_tiles) issue(t + 2, smem);
+      if (t + 1 < wave_tiles)
+        tile_step<QK, DV, CAUSAL, STAGE, KPART>(st, qf, kl, va, smem, (t + 1) * BN, t + 1 >= mask_from, qrow, off,
+                                                p.Skv, c, hl, has_ks);
     }
 
-    float mx = -INFINITY;
+    // epilogue: O = O^T / l, LSE = m_ref * scale + ln l
+    const float l_tot = xor32_sum(st.l);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < p.Sq) {
+      char* ob = (char*)p.o + (((size_t)b * p.Sq + qrow) * p.Hq + h) * (size_t)VROWB;
 #pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
+      for (int db = 0; db < DV / 32; db++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[kb][v]);
-    mx = xor32_max(mx);
-    float neg;
-    const float alpha = softmax_rescale(st, mx, c, neg);
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const float e = exp2_fast(fmaf(s[kb][v], c, neg));
-        s[kb][v] = e;
-        rs += e;
-      }
-    st.l = st.l * alpha + rs;
-#pragma unroll
-    for (int d = 0; d < DV / 32; d++) o[d] *= alpha;
-
-    // O^T += V^T . P^T
-    const FA_LDS char* vt = cur + KPART;
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; kb++)
-#pragma unroll
-      for (int tp = 0; tp < 2; tp++) {
-        const i32x4_t pb = {pack_bf16(s[kb][8 * tp + 0], s[kb][8 * tp + 1]), pack_bf16(s[kb][8 * tp + 2], s[kb][8 * tp + 3]),
-                            pack_bf16(s[kb][8 * tp + 4], s[kb][8 * tp + 5]), pack_bf16(s[kb][8 * tp + 6], s[kb][8 * tp + 7])};
-        const int row0 = 32 * kb + 16 * tp + 4 * (g >> 1) + (i16 >> 2);
-#pragma unroll
-        for (int db = 0; db < DV / 32; db++) {
-          const int col = 32 * db + 16 * (g & 1) + 4 * (i16 & 3);
-          i32x2_t part[2];
-#pragma unroll
-          for (int u = 0; u < 2; u++) {
-            const int row = row0 + 8 * u;
-            const uint32_t sw = DV == 128 ? swz256(row) : swz_half(row);
-            part[u] = lds_tr16(vt + row * VROWB + ((((uint32_t)col >> 3) ^ sw) << 4) + (((col >> 2) & 1) << 3));
-          }
-          o[db] = mfma32x32x16_bf16(cat(part[0], part[1]), pb, o[db]);
+        for (int j = 0; j < 4; j++) {
+          const int d = 32 * db + 8 * j + 4 * hl;
+          const i32x2_t wv = {pack_bf16(st.o[db][4 * j] * inv, st.o[db][4 * j + 1] * inv),
+                              pack_bf16(st.o[db][4 * j + 2] * inv, st.o[db][4 * j + 3] * inv)};
+          *(i32x2_t*)(ob + d * 2) = wv;
         }
-      }
-  }
-
-  // epilogue: O = O^T / l, LSE = m * scale + ln l
-  const float l_tot = xor32_sum(st.l);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < p.Sq) {
-    char* ob = (char*)p.o + (((size_t)b * p.Sq + qrow) * p.Hq + h) * (size_t)VROWB;
-#pragma unroll
-    for (int db = 0; db < DV / 32; db++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int d = 32 * db + 8 * j + 4 * hl;
-        i32x2_t w = {pack_bf16(o[db][4 * j] * inv, o[db][4 * j + 1] * inv), pack_bf16(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv)};
-        *(i32x2_t*)(ob + d * 2) = w;
-      }
-    if (p.lse && hl == 0)
-      p.lse[((size_t)b * p.Hq + h) * p.Sq + qrow] = l_tot > 0.f ? st.m * p.scale + logf(l_tot) : -INFINITY;
+      if (p.lse && hl == 0)
+        p.lse[((size_t)b * p.Hq + h) * p.Sq + qrow] = l_tot > 0.f ? st.m_ref * p.scale + logf(l_tot) : -INFINITY;
+    }
   }
 }
 
-// ------------------------------------------------------------------------------------
-// fp32 prefill: v_mfma_f32_32x32x2_f32 for both products, K/V tiles of 32 keys staged
-// through LDS with ordinary loads (one stage).  S^T MFMA number c contracts head-dim
-// columns c (lanes 0-31) and c + D/2 (lanes 32-63).
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p, int n_qblocks) {
-  constexpr int BNF = 32, LD = D + 4;
-  __shared__ float kt[BNF][LD];
-  __shared__ float vt[BNF][LD];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int BH = p.B * p.Hq;
-  const int rank = blockIdx.x / BH, bh = blockIdx.x % BH;
-  const int qb = CAUSAL ? (n_qblocks - 1 - rank) : rank;
-  const int b = bh / p.Hq, h = bh % p.Hq, kvh = h / (p.Hq / p.Hkv);
-  const int q0 = qb * BM, off = p.Skv - p.Sq;
-  int kv_end = p.Skv;
-  if (CAUSAL) kv_end = max(0, min(p.Skv, min(q0 + BM, p.Sq) - 1 + off + 1));
-  const int n_tiles = (kv_end + BNF - 1) / BNF;
-  const int qrow = q0 + 32 * wave + l32, qrow_c = min(qrow, p.Sq - 1);
-  const float c = p.scale * kLog2e;
-
-  float q[D / 2];
-  {
-    const float* qp = (const float*)p.q + (((size_t)b * p.Sq + qrow_c) * p.Hq + h) * D + (D / 2) * hl;
-#pragma unroll
-    for (int i = 0; i < D / 2; i += 4) {
-      f32x4_t x = *(const f32x4_t*)(qp + i);
-      q[i] = x.x; q[i + 1] = x.y; q[i + 2] = x.z; q[i + 3] = x.w;
-    }
-  }
-  RowState st{-INFINITY, 0.f};
-  f32x16_t o[D / 32];
-#pragma unroll
-  for (int d = 0; d < D / 32; d++) o[d] = f32x16_t{};
-
-  for (int t = 0; t < n_tiles; t++) {
-    __syncthreads();
-    for (int e = tid * 4; e < BNF * D; e += 256 * 4) {
-      const int row = e / D, col = e % D;
-      const int key = min(t * BNF + row, p.Skv - 1);
-      const size_t gi = (((size_t)b * p.Skv + key) * p.Hkv + kvh) * D + col;
-      *(f32x4_t*)&kt[row][col] = *(const f32x4_t*)((const float*)p.k + gi);
-      *(f32x4_t*)&vt[row][col] = *(const f32x4_t*)((const float*)p.v + gi);
-    }
-    __syncthreads();
-    f32x16_t s{};
-#pragma unroll
-    for (int cc = 0; cc < D / 2; cc++) s = mfma32x32x2_f32(kt[l32][cc + (D / 2) * hl], q[cc], s);
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int key = t * BNF + 8 * (v >> 2) + 4 * hl + (v & 3);
-      const bool vis = key < p.Skv && (!CAUSAL || key <= qrow + off);
-      s[v] = vis ? s[v] : -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; v++) mx = fmaxf(mx, s[v]);
-    mx = xor32_max(mx);
-    float neg;
-    const float alpha = softmax_rescale(st, mx, c, neg);
-    float rs = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
-      s[v] = exp2_fast(fmaf(s[v], c, neg));
-      rs += s[v];
-    }
-    st.l = st.l * alpha + rs;
-#pragma unroll
-    for (int d = 0; d < D / 32; d++) o[d] *= alpha;
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int key = 8 * (v >> 2) + 4 * hl + (v & 3);
-#pragma unroll
-      for (int d = 0; d < D / 32; d++) o[d] = mfma32x32x2_f32(vt[key][32 * d + l32], s[v], o[d]);
-    }
-  }
-  const float l_tot = xor32_sum(st.l);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < p.Sq) {
-    float* op = (float*)p.o + (((size_t)b * p.Sq + qrow) * p.Hq + h) * D;
-#pragma unroll
-    for (int d = 0; d < D / 32; d++)
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        *(f32x4_t*)(op + 32 * d + 8 * j + 4 * hl) =
-            f32x4_t{o[d][4 * j] * inv, o[d][4 * j + 1] * inv, o[d][4 * j + 2] * inv, o[d][4 * j + 3] * inv};
-    if (p.lse && hl == 0)
-      p.lse[((size_t)b * p.Hq + h) * p.Sq + qrow] = l_tot > 0.f ? st.m * p.scale + logf(l_tot) : -INFINITY;
-  }
-}
-
-int grid_of(const PrefillArgs& a, int& n_qblocks) {
+int items(const PrefillArgs& a, int& n_qblocks) {
   n_qblocks = (a.Sq + BM - 1) / BM;
-  return n_qblocks * a.B * a.Hq;
+  const int per_head = a.causal ? (n_qblocks + 1) / 2 : n_qblocks;
+  return per_head * a.B * a.Hq;
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s) {
   int nqb;
-  const int grid = grid_of(a, nqb);
+  const int grid = items(a, nqb);
   if (grid == 0) return hipSuccess;
   if (D == 128) {
     if (a.causal) prefill_kernel<QkBf16<128>, 128, true><<<grid, 256, 0, s>>>(a, nqb);
@@ -448,23 +435,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t s) {
-  int nqb;
-  const int grid = grid_of(a, nqb);
-  if (grid == 0) return hipSuccess;
-  if (D == 128) {
-    if (a.causal) prefill_f32_kernel<128, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_f32_kernel<128, false><<<grid, 256, 0, s>>>(a, nqb);
-  } else {
-    if (a.causal) prefill_f32_kernel<64, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_f32_kernel<64, false><<<grid, 256, 0, s>>>(a, nqb);
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, hipStream_t s) {
   int nqb;
-  const int grid = grid_of(a, nqb);
+  const int grid = items(a, nqb);
   if (grid == 0) return hipSuccess;
   if (nope_fp8) {
     if (a.causal) prefill_kernel<QkMla<true>, 128, true><<<grid, 256, 0, s>>>(a, nqb);

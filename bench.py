@@ -177,6 +177,27 @@ def cpu_baseline(w, lens, budget_s: float):
             "sample": f"{len(sel)} whole sequences (lengths {sel[:4]}...)", "seconds": round(t_used, 2)}
 
 
+# ------------------------------------------------------------------------------- counters
+
+def copy_calibration(steps: int):
+    """A plain copy of exactly 1 GiB (reads 1 GiB, writes 1 GiB) per launch: what FETCH_SIZE and
+    WRITE_SIZE read for it gives the factor that turns those counters into bytes."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": round(dt * 1e3, 4),
+                      "GB_per_s": round(2 * n / dt / 1e9, 1)}), flush=True)
+
+
 # ------------------------------------------------------------------------------- main
 
 def main():
@@ -189,6 +210,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU sample")
     ap.add_argument("--traffic", default=None, help="JSON file with HBM traffic per launch from rocprofv3 counters")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy instead (scales FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is a design note, "
@@ -197,6 +220,9 @@ def main():
 
     import torch
     from workloads import workload
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     w = workload(args.workload)
     torch.cuda.set_device(0)
     step, lens, keep = setup(w)
