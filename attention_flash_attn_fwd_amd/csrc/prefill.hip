@@ -107,13 +107,12 @@ struct QkBf16 {
     const char* base = (const char*)p.k + (((size_t)b * p.Skv + key0) * p.Hkv + kvh) * (size_t)ROWB;
     s.dma.issue(base, p.Hkv * ROWB, min(BN, p.Skv - key0), dst, wave, lane);
   }
-  template <int OFF>
-  __device__ static void scores(const QFrag& q, const Lane& s, const FA_LDS char* smem, int kb, int hl,
+  __device__ static void scores(const QFrag& q, const Lane& s, const FA_LDS char* stage, int kb, int hl,
                                 f32x16_t& acc, bool /*has_kscale*/) {
     (void)hl;
     acc = f32x16_t{};
 #pragma unroll
-    for (int c = 0; c < D / 16; c++) acc = mfma32x32x16_bf16(lds_b128(smem + s.ka[c] + (OFF + kb * 32 * ROWB)), q.c[c], acc);
+    for (int c = 0; c < D / 16; c++) acc = mfma32x32x16_bf16(lds_b128(stage + s.ka[c] + kb * 32 * ROWB), q.c[c], acc);
   }
 };
 
@@ -196,29 +195,28 @@ struct QkMla {
       dma4_buf(r, dst + KS, (uint32_t)min(lane, valid - 1) * p.Hq * 4);
     }
   }
-  template <int OFF>
-  __device__ static void scores(const QFrag& q, const Lane& s, const FA_LDS char* smem, int kb, int hl,
+  __device__ static void scores(const QFrag& q, const Lane& s, const FA_LDS char* stage, int kb, int hl,
                                 f32x16_t& acc, bool has_kscale) {
     (void)hl;
     f32x16_t sn{};
     if constexpr (FP8) {
 #pragma unroll
       for (int c = 0; c < 2; c++) {
-        const i32x4_t lo = lds_b128(smem + s.na[2 * c] + (OFF + kb * 32 * NROWB));
-        const i32x4_t hi = lds_b128(smem + s.na[2 * c + 1] + (OFF + kb * 32 * NROWB));
+        const i32x4_t lo = lds_b128(stage + s.na[2 * c] + kb * 32 * NROWB);
+        const i32x4_t hi = lds_b128(stage + s.na[2 * c + 1] + kb * 32 * NROWB);
         sn = mfma32x32x64_e4m3(i32x8_t{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w}, q.n8[c], sn);
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < 8; c++) sn = mfma32x32x16_bf16(lds_b128(smem + s.na[c] + (OFF + kb * 32 * NROWB)), q.n16[c], sn);
+      for (int c = 0; c < 8; c++) sn = mfma32x32x16_bf16(lds_b128(stage + s.na[c] + kb * 32 * NROWB), q.n16[c], sn);
     }
     f32x16_t sr{};
 #pragma unroll
-    for (int c = 0; c < 4; c++) sr = mfma32x32x16_bf16(lds_b128(smem + s.ra[c] + (OFF + kb * 32 * 128)), q.r[c], sr);
+    for (int c = 0; c < 4; c++) sr = mfma32x32x16_bf16(lds_b128(stage + s.ra[c] + kb * 32 * 128), q.r[c], sr);
     // this lane holds keys 32kb + 8j + 4hl + i in register 4j + i
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const f32x4_t ks = has_kscale ? lds_f32x4(smem + s.sa + (OFF + (32 * kb + 8 * j) * 4)) : f32x4_t{1.f, 1.f, 1.f, 1.f};
+      const f32x4_t ks = has_kscale ? lds_f32x4(stage + s.sa + (32 * kb + 8 * j) * 4) : f32x4_t{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[4 * j + i] = fmaf(sn[4 * j + i], q.qs * ks[i], sr[4 * j + i]);
     }
@@ -236,14 +234,14 @@ struct RowAcc {
   float l;              // lane-partial sum of the bf16-rounded P of this lane's keys
 };
 
-template <class QK, int DV, bool CAUSAL, int OFF, int KPART>
+template <class QK, int DV, bool CAUSAL, int KPART>
 __device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFrag& q, const typename QK::Lane& ks,
-                                          const uint32_t (&va)[2][DV / 32], const FA_LDS char* smem, int key0,
+                                          const uint32_t (&va)[2][DV / 32], const FA_LDS char* stage, int key0,
                                           bool masked, int qrow, int off, int Skv, float c, int hl, bool has_ks) {
   constexpr int VROWB = DV * 2;
   f32x16_t s[BN / 32];
 #pragma unroll
-  for (int kb = 0; kb < BN / 32; kb++) QK::template scores<OFF>(q, ks, smem, kb, hl, s[kb], has_ks);
+  for (int kb = 0; kb < BN / 32; kb++) QK::scores(q, ks, stage, kb, hl, s[kb], has_ks);
   if (masked) {
 #pragma unroll
     for (int kb = 0; kb < BN / 32; kb++)
@@ -289,10 +287,9 @@ __device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFr
     for (int tp = 0; tp < 2; tp++)
 #pragma unroll
       for (int db = 0; db < DV / 32; db++) {
-        constexpr int base = OFF + KPART;
-        const int rows = (32 * kb + 16 * tp) * VROWB;
-        const i32x2_t lo = lds_tr16(smem + va[0][db] + (base + rows));
-        const i32x2_t hi = lds_tr16(smem + va[1][db] + (base + rows));
+        const int rows = KPART + (32 * kb + 16 * tp) * VROWB;
+        const i32x2_t lo = lds_tr16(stage + va[0][db] + rows);
+        const i32x2_t hi = lds_tr16(stage + va[1][db] + rows);
         st.o[db] = mfma32x32x16_bf16(cat(lo, hi), pb[kb][tp], st.o[db]);
       }
 }
@@ -304,8 +301,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qb
   constexpr int KPART = (QK::KBYTES + 1023) / 1024 * 1024;
   constexpr int VROWB = DV * 2;
   constexpr int STAGE = KPART + BN * VROWB;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE];
-  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  // One LDS object per stage: the compiler then sees that reads of one stage cannot alias
+  // the direct copies into the other and does not wait for those copies before reading.
+  __shared__ __attribute__((aligned(1024))) char stage0_raw[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1_raw[STAGE];
+  FA_LDS char* stage0 = (FA_LDS char*)stage0_raw;
+  FA_LDS char* stage1 = (FA_LDS char*)stage1_raw;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hl = lane >> 5;
@@ -377,20 +378,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qb
     st.l = 0.f;
 
     if (bi > 0) barrier();  // every wave is done reading the previous block's last stage
-    if (n_tiles > 0) issue(0, smem);
+    if (n_tiles > 0) issue(0, stage0);
     for (int t = 0; t < n_tiles; t += 2) {
       wait_vmcnt<0>();
       barrier();
-      if (t + 1 < n_tiles) issue(t + 1, smem + STAGE);
+      if (t + 1 < n_tiles) issue(t + 1, stage1);
       if (t < wave_tiles)
-        tile_step<QK, DV, CAUSAL, 0, KPART>(st, qf, kl, va, smem, t * BN, t >= mask_from, qrow, off, p.Skv, c, hl, has_ks);
+        tile_step<QK, DV, CAUSAL, KPART>(st, qf, kl, va, stage0, t * BN, t >= mask_from, qrow, off, p.Skv, c, hl, has_ks);
       if (t + 1 >= n_tiles) break;
       wait_vmcnt<0>();
       barrier();
-      if (t + 2 < n_tiles) issue(t + 2, smem);
+      if (t + 2 < n_tiles) issue(t + 2, stage0);
       if (t + 1 < wave_tiles)
-        tile_step<QK, DV, CAUSAL, STAGE, KPART>(st, qf, kl, va, smem, (t + 1) * BN, t + 1 >= mask_from, qrow, off,
-                                                p.Skv, c, hl, has_ks);
+        tile_step<QK, DV, CAUSAL, KPART>(st, qf, kl, va, stage1, (t + 1) * BN, t + 1 >= mask_from, qrow, off, p.Skv, c,
+                                         hl, has_ks);
     }
 
     // epilogue: O = O^T / l, LSE = m_ref * scale + ln l
