@@ -10,6 +10,8 @@
 // Both products use v_mfma_f32_16x16x32_bf16 in transposed form (S^T = K.Q^T and
 // O^T = V^T.P^T); the 16 MFMA columns hold query heads (the Hq/Hkv heads of a GQA group,
 // or 16 of the MLA heads).
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -19,18 +21,25 @@ namespace {
 constexpr int TK = 32;  // keys per tile
 
 // ------------------------------------------------------------------------------------
-// GQA decode split: one wave per workgroup = one split of one (batch, kv head); the wave
-// owns a private STAGES-deep LDS ring of K and V tiles (32 keys x 128 bf16 each), filled by
-// direct global->LDS loads, so no workgroup barrier is needed.
+// GQA decode split: one wave per workgroup = one split of one (batch, kv head).  K goes
+// from global memory straight into the MFMA A-operand registers (buffer loads; rows past
+// the sequence read as zero), two register slots deep; only V, which must be read
+// transposed, is staged in LDS by direct loads (two stages, 16 KiB per wave).  The small
+// LDS footprint lets ~10 waves share a CU, which keeps enough bytes in flight to stream
+// the cache at HBM rate.
 
 template <int G>
 __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
-  constexpr int D = 128, ROWB = 256, TILE = TK * ROWB, STAGES = 3;
-  constexpr int OPS = 2 * TILE / 1024;  // vector-memory instructions per tile (K + V)
-  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * 2 * TILE];
-  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+  constexpr int D = 128, ROWB = 256, VTILE = TK * ROWB;
+  constexpr int KOPS = 8, VOPS = VTILE / 1024;  // vector-memory instructions per tile
+  // one LDS object per stage, selected at compile time (see the prefill kernel)
+  __shared__ __attribute__((aligned(1024))) char v0_raw[VTILE];
+  __shared__ __attribute__((aligned(1024))) char v1_raw[VTILE];
+  FA_LDS char* const vst[2] = {(FA_LDS char*)v0_raw, (FA_LDS char*)v1_raw};
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // kv head fastest: the workgroups of one (batch, split) run together and read each
+  // token's kv heads, which are adjacent in the cache, as one contiguous stretch
+  const int kvh = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
   const int L = min(max(a.kv_lens[b], 0), a.max_len);
   const int start = split * a.chunk;
   if (start >= L) return;
@@ -39,61 +48,85 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 
   const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
   const float c = a.scale * kLog2e;
+  const uint32_t rstride = (uint32_t)a.Hkv * ROWB;  // bytes between consecutive keys
 
+  // Q^T as the B operand: column l16 = query head kvh*G + l16 (zero past the group),
+  // k = head-dim 32cc + 8g .. +7
   i32x4_t qf[D / 32];
   {
     const int hq = kvh * G + (l16 < G ? l16 : 0);
     const char* qp = (const char*)a.q + ((size_t)b * a.Hq + hq) * ROWB;
 #pragma unroll
     for (int cc = 0; cc < D / 32; cc++) {
-      i32x4_t x = *(const i32x4_t*)(qp + cc * 64 + g * 16);
+      const i32x4_t x = *(const i32x4_t*)(qp + cc * 64 + g * 16);
       qf[cc] = l16 < G ? x : i32x4_t{};
     }
   }
-
-  auto issue = [&](int t) {
-    FA_LDS char* dst = smem + (t % STAGES) * 2 * TILE;
-    const int key0 = start + t * TK;
+  const char* kbase = (const char*)a.k + ((size_t)b * a.max_len * a.Hkv + kvh) * ROWB;
+  const char* vbase = (const char*)a.v + ((size_t)b * a.max_len * a.Hkv + kvh) * ROWB;
+  // K A operand of key block kb: row 16kb + l16, head-dim chunk 4cc + g
+  const uint32_t koff0 = l16 * rstride + g * 16, koff1 = (16 + l16) * rstride + g * 16;
+  // V copy: LDS row 4i + g holds key row 4i + g with 16-byte chunks XOR-permuted
+  uint32_t voff[VOPS];
 #pragma unroll
-    for (int i = 0; i < TILE / 1024; i++) {
-      const int row = i * 4 + (lane >> 4);
-      const int lch = (lane & 15) ^ swz256(row);
-      const int key = min(key0 + row, L - 1);
-      const size_t gi = (((size_t)b * a.max_len + key) * a.Hkv + kvh) * ROWB + lch * 16;
-      dma16((const char*)a.k + gi, dst + i * 1024);
-      dma16((const char*)a.v + gi, dst + TILE + i * 1024);
+  for (int i = 0; i < VOPS; i++) {
+    const uint32_t row = 4 * i + g;
+    voff[i] = row * rstride + ((l16 ^ swz256(row)) << 4);
+  }
+  // transposing V reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4) .. +3.  The column
+  // slab of block db is chunk pair db: swizzled to pair db ^ (swz >> 1), chunk (l16%4)/2 of
+  // the pair flipped by swz & 1.
+  uint32_t vrow[2], vpair[2];
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const uint32_t row = 16 * u + 4 * g + (l16 >> 2), sw = swz256(row);
+    vrow[u] = row * ROWB + (((((l16 & 3) >> 1) ^ (sw & 1))) << 4) + ((l16 & 1) << 3);
+    vpair[u] = sw >> 1;
+  }
+
+  i32x4_t kf[2][2][D / 32];
+  auto issue_k = [&](int t, i32x4_t (&dst)[2][D / 32]) {
+    const int key0 = start + t * TK;
+    const auto r = make_rsrc(kbase + (size_t)key0 * rstride, (uint32_t)(end - key0) * rstride);
+#pragma unroll
+    for (int cc = 0; cc < D / 32; cc++) {
+      dst[0][cc] = __builtin_amdgcn_raw_buffer_load_b128(r, koff0 + cc * 64, 0, 0);
+      dst[1][cc] = __builtin_amdgcn_raw_buffer_load_b128(r, koff1 + cc * 64, 0, 0);
+    }
+  };
+  auto issue_v = [&](int t, FA_LDS char* dst) {
+    const int key0 = start + t * TK, valid = min(TK, end - key0);
+    const auto r = make_rsrc(vbase + (size_t)key0 * rstride, (uint32_t)(valid - 1) * rstride + ROWB);
+    if (valid == TK) {
+#pragma unroll
+      for (int i = 0; i < VOPS; i++) dma16_buf(r, dst + i * 1024, voff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VOPS; i++) {
+        const uint32_t row = 4 * i + g, rc = min(row, (uint32_t)(valid - 1));
+        dma16_buf(r, dst + i * 1024, rc * rstride + ((l16 ^ swz256(row)) << 4));
+      }
     }
   };
 
-  RowState st{-INFINITY, 0.f};
+  float m_ref = -INFINITY, neg = 0.f, l = 0.f;
   f32x4_t o[D / 16];
 #pragma unroll
   for (int d = 0; d < D / 16; d++) o[d] = f32x4_t{};
 
-#pragma unroll
-  for (int t = 0; t < STAGES - 1; t++)
-    if (t < n_tiles) issue(t);
-
-  for (int t = 0; t < n_tiles; t++) {
-    if (t + STAGES - 1 < n_tiles) issue(t + STAGES - 1);
-    const int after = min(STAGES - 1, n_tiles - 1 - t);  // tiles issued after tile t
-    if (after >= 2) wait_vmcnt<2 * OPS>();
-    else if (after == 1) wait_vmcnt<OPS>();
-    else wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-
-    const FA_LDS char* kt = smem + (t % STAGES) * 2 * TILE;
-    const FA_LDS char* vt = kt + TILE;
+  // tile t: K(t) in kf[t & 1] (issued two tiles earlier), V(t) in vst[t & 1] (one tile
+  // earlier).  Issue order per tile: V(t+1), then K(t+2) once K(t) has been consumed.
+  auto tile = [&](auto SLOT, int t) {
+    constexpr int sl = decltype(SLOT)::value;
+    if (t + 1 < n_tiles) issue_v(t + 1, vst[sl ^ 1]);
     f32x4_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
-      const int row = 16 * kb + l16;
-      const FA_LDS char* r = kt + row * ROWB;
-      const uint32_t sw = swz256(row);
       s[kb] = f32x4_t{};
 #pragma unroll
-      for (int cc = 0; cc < D / 32; cc++) s[kb] = mfma16x16x32_bf16(lds_b128(r + (((4 * cc + g) ^ sw) << 4)), qf[cc], s[kb]);
+      for (int cc = 0; cc < D / 32; cc++) s[kb] = mfma16x16x32_bf16(kf[sl][kb][cc], qf[cc], s[kb]);
     }
+    if (t + 2 < n_tiles) issue_k(t + 2, kf[sl]);
     const int key0 = start + t * TK;
     if (key0 + TK > end) {
 #pragma unroll
@@ -105,35 +138,48 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = xor32_max(xor16_max(mx));
-    float neg;
-    const float alpha = softmax_rescale(st, mx, c, neg);
-    float rs = 0.f;
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_ref * c + 8.f)) {  // lazy rescale (P <= 2^8)
+      const float m_new = fmaxf(m_ref, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast((m_ref - m_use) * c);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < D / 16; d++) o[d] *= alpha;
+      m_ref = m_new;
+      neg = -m_use * c;
+    }
+    float e[8];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const float e = exp2_fast(fmaf(s[kb][v], c, neg));
-        s[kb][v] = e;
-        rs += e;
-      }
-    st.l = st.l * alpha + rs;
-    const i32x4_t pb = {pack_bf16(s[0][0], s[0][1]), pack_bf16(s[0][2], s[0][3]), pack_bf16(s[1][0], s[1][1]),
-                        pack_bf16(s[1][2], s[1][3])};
+      for (int v = 0; v < 4; v++) e[4 * kb + v] = exp2_fast(fmaf(s[kb][v], c, neg));
+    const i32x4_t pb = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
+#pragma unroll
+    for (int i = 0; i < 4; i++) l = dot2_bf16(pb[i], kBf16PairOne, l);
+    // V(t) must have landed: later vector-memory ops are K(t+1), V(t+1), K(t+2)
+    if (t + 2 < n_tiles) wait_vmcnt<2 * KOPS + VOPS>();
+    else if (t + 1 < n_tiles) wait_vmcnt<KOPS + VOPS>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    const FA_LDS char* vt = vst[sl];
 #pragma unroll
     for (int db = 0; db < D / 16; db++) {
-      o[db] *= alpha;
-      const int col = 16 * db + 4 * (l16 & 3);
-      i32x2_t part[2];
-#pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int row = 16 * u + 4 * g + (l16 >> 2);
-        part[u] = lds_tr16(vt + row * ROWB + ((((uint32_t)col >> 3) ^ swz256(row)) << 4) + (((col >> 2) & 1) << 3));
-      }
-      o[db] = mfma16x16x32_bf16(cat(part[0], part[1]), pb, o[db]);
+      const i32x2_t lo = lds_tr16(vt + vrow[0] + ((db ^ vpair[0]) << 5));
+      const i32x2_t hi = lds_tr16(vt + vrow[1] + ((db ^ vpair[1]) << 5));
+      o[db] = mfma16x16x32_bf16(cat(lo, hi), pb, o[db]);
     }
+  };
+
+  issue_k(0, kf[0]);
+  issue_v(0, vst[0]);
+  if (1 < n_tiles) issue_k(1, kf[1]);
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= n_tiles) break;
+    tile(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  const float l_tot = xor32_sum(xor16_sum(st.l));
+  const float l_tot = xor32_sum(xor16_sum(l));
   if (l16 < G) {
     const int hq = kvh * G + l16;
     const size_t pidx = ((size_t)b * a.Hq + hq) * a.n_split + split;
@@ -141,7 +187,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < D / 16; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
     if (g == 0) {
-      a.part_ml[2 * pidx] = st.m;
+      a.part_ml[2 * pidx] = m_ref;
       a.part_ml[2 * pidx + 1] = l_tot;
     }
   }
@@ -297,8 +343,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
 
 SplitPlan gqa_decode_plan(int B, int Hq, int max_len) {
   (void)Hq;
-  int chunk = 256;
-  // keep at least ~2048 waves in flight for small batches
+  int chunk = 1024;
+  // keep at least ~2048 waves for small batches
   while (chunk > TK && (long)B * 8 * ((max_len + chunk - 1) / chunk) < 2048) chunk /= 2;
   SplitPlan p;
   p.chunk = chunk;
@@ -327,7 +373,7 @@ size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split) {
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  dim3 grid(a.n_split, a.Hkv, a.B);
+  dim3 grid(a.Hkv, a.n_split, a.B);
   switch (G) {
 #define FA_G(n) case n: gqa_decode_split<n><<<grid, 64, 0, s>>>(a); break;
     FA_G(1) FA_G(2) FA_G(3) FA_G(4) FA_G(5) FA_G(6) FA_G(7) FA_G(8)
