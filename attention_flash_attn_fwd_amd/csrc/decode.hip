@@ -194,20 +194,36 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// MLA decode split: workgroup = H/16 waves sharing one LDS ring of latent tiles
-// (32 keys x 576 bf16 = 36 KiB, two stages); wave w owns heads 16w..16w+15.  The tile feeds
-// S^T over all 576 columns and, through transposing reads of its first 512 columns,
-// O^T = V^T.P^T: the latent cache is read from HBM once.
+// MLA decode split: one workgroup of 8 waves per (split, batch); wave w owns heads
+// 16w .. 16w+15 as the 16 MFMA columns of v_mfma_f32_16x16x32_bf16 (S^T = K.Q^T, then
+// O^T = V^T.P^T).  The 576-wide latent tile (32 keys) is copied into a three-stage LDS ring
+// by direct loads and read by every wave: all 576 columns feed S^T and, through
+// transposing reads, its first 512 columns feed O^T, so the cache is read from HBM once.
+// Q^T (72 VGPRs) and O^T (128) stay in registers at two waves per SIMD, which leaves no
+// room for deep read-ahead: LDS fragments are read in small groups.
+//
+// In LDS a latent row occupies 1280 bytes (five 256-byte bank rows; the last 128 bytes are
+// padding), so every row starts on the same bank and the 4-bit XOR swizzle of 256-byte rows
+// applies within each group of 16 chunks.
 
-constexpr int MLA_DK = 576, MLA_DV = 512, MLA_ROWB = 1152, MLA_TILE = TK * MLA_ROWB;
+constexpr int MLA_DK = 576, MLA_DV = 512, MLA_ROWB = 1152, MLA_LROWB = 1280;
+constexpr int MLA_LTILE = TK * MLA_LROWB;             // 40 KiB per stage
+constexpr int MLA_NW = 8, MLA_NS = 3;
+constexpr int MLA_OPS = MLA_LTILE / 1024 / MLA_NW;    // direct copies per wave per tile
+static_assert(MLA_LTILE % (1024 * MLA_NW) == 0, "tile copy split");
 
-__global__ __launch_bounds__(512) void mla_decode_split(DecodeArgs a) {
-  constexpr int STAGES = 2;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[STAGES * MLA_TILE];
-  FA_LDS char* smem = (FA_LDS char*)smem_raw;
+// physical 16-byte chunk of logical chunk lc in LDS row `row`
+__device__ __forceinline__ uint32_t mla_chunk(uint32_t row, uint32_t lc) {
+  return (lc & ~15u) | ((lc & 15u) ^ swz256(row));
+}
+
+__global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0_raw[MLA_LTILE];
+  __shared__ __attribute__((aligned(1024))) char st1_raw[MLA_LTILE];
+  __shared__ __attribute__((aligned(1024))) char st2_raw[MLA_LTILE];
+  FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw};
 
   const int split = blockIdx.x, b = blockIdx.y;
-  const int nw = blockDim.x >> 6;
   const int L = min(max(a.kv_lens[b], 0), a.max_len);
   const int start = split * a.chunk;
   if (start >= L) return;  // uniform over the workgroup
@@ -216,49 +232,66 @@ __global__ __launch_bounds__(512) void mla_decode_split(DecodeArgs a) {
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int h = 16 * wave + l16;
+  const bool hvalid = h < a.Hq;
   const float c = a.scale * kLog2e;
 
+  // Q^T as the B operand: column l16 = head h, k = latent column 32cc + 8g .. +7
   i32x4_t qf[MLA_DK / 32];
   {
-    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + h) * MLA_ROWB;
+    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * MLA_ROWB;
 #pragma unroll
     for (int cc = 0; cc < MLA_DK / 32; cc++) qf[cc] = *(const i32x4_t*)(qp + cc * 64 + g * 16);
   }
-
-  auto issue = [&](int t) {
-    FA_LDS char* dst = smem + (t % STAGES) * MLA_TILE;
-    const int key0 = start + t * TK;
-    for (int blk = wave; blk < MLA_TILE / 1024; blk += nw) {
-      const int o = blk * 1024 + lane * 16;
-      const int row = o / MLA_ROWB;
-      const int lch = ((o % MLA_ROWB) >> 4) ^ swz_half(row);
-      const int key = min(key0 + row, L - 1);
-      dma16((const char*)a.k + ((size_t)b * a.max_len + key) * MLA_ROWB + lch * 16, dst + blk * 1024);
+  const char* kv = (const char*)a.k + (size_t)b * a.max_len * MLA_ROWB;
+  // direct copy of a tile: LDS byte o = blk*1024 + 16*lane is row o / 1280, physical chunk
+  // (o % 1280) / 16; it receives the logical chunk that maps there (padding slots receive
+  // a duplicate of chunk 71 and are never read)
+  auto issue = [&](int t, FA_LDS char* dst) {
+    const int key0 = start + t * TK, valid = min(TK, end - key0);
+    const auto r = make_rsrc(kv + (size_t)key0 * MLA_ROWB, (uint32_t)valid * MLA_ROWB);
+#pragma unroll
+    for (int i = 0; i < MLA_OPS; i++) {
+      const uint32_t blk = i * MLA_NW + wave, o = blk * 1024 + lane * 16;
+      const uint32_t row = o / MLA_LROWB, pc = (o % MLA_LROWB) >> 4;
+      const uint32_t lc = min(mla_chunk(row, pc), (uint32_t)(MLA_ROWB / 16 - 1));
+      const uint32_t rc = min(row, (uint32_t)(valid - 1));  // rows past the sequence repeat its last row
+      dma16_buf(r, dst + blk * 1024, rc * MLA_ROWB + lc * 16);
     }
   };
+  const uint32_t ksw = swz256(l16);  // S^T A operand: row 16kb + l16, logical chunk 4cc + g
+  uint32_t vrow[2], vsw[2];         // V^T reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4)
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const uint32_t row = 16 * u + 4 * g + (l16 >> 2);
+    vrow[u] = row * MLA_LROWB + ((l16 & 1) << 3);
+    vsw[u] = swz256(row);
+  }
+  const uint32_t vc0 = (l16 & 3) >> 1;  // logical chunk of column block db: 2db + vc0
 
-  RowState st{-INFINITY, 0.f};
+  float m_ref = -INFINITY, neg = 0.f, l = 0.f;
   f32x4_t o[MLA_DV / 16];
 #pragma unroll
   for (int d = 0; d < MLA_DV / 16; d++) o[d] = f32x4_t{};
 
-  issue(0);
-  for (int t = 0; t < n_tiles; t++) {
-    wait_vmcnt<0>();
+  auto tile = [&](auto SLOT, int t) {
+    constexpr int sl = decltype(SLOT)::value;
+    // tile t landed (the copies of tile t+1 may still be in flight), and every wave is
+    // done with tile t-1, whose stage is refilled with tile t+2 below
+    if (t + 1 < n_tiles) wait_vmcnt<MLA_OPS>();
+    else wait_vmcnt<0>();
     barrier();
-    if (t + 1 < n_tiles) issue(t + 1);
-    const FA_LDS char* kt = smem + (t % STAGES) * MLA_TILE;
-
-    f32x4_t s[2];
+    if (t + 2 < n_tiles) issue(t + 2, st[(sl + 2) % MLA_NS]);
+    const FA_LDS char* kt = st[sl];
+    f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-      const int row = 16 * kb + l16;
-      const FA_LDS char* r = kt + row * MLA_ROWB;
-      const uint32_t sw = swz_half(row);
-      s[kb] = f32x4_t{};
+    for (int cc = 0; cc < MLA_DK / 32; cc++) {
+      const uint32_t lc = 4 * cc + g;
 #pragma unroll
-      for (int cc = 0; cc < MLA_DK / 32; cc++)
-        s[kb] = mfma16x16x32_bf16(lds_b128(r + (((4 * cc + g) ^ sw) << 4)), qf[cc], s[kb]);
+      for (int kb = 0; kb < 2; kb++) {
+        const i32x4_t ka = lds_b128(kt + (16 * kb + l16) * MLA_LROWB + (((lc & ~15u) | ((lc & 15u) ^ ksw)) << 4));
+        s[kb] = mfma16x16x32_bf16(ka, qf[cc], s[kb]);
+      }
+      if (cc % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
     const int key0 = start + t * TK;
     if (key0 + TK > end) {
@@ -271,42 +304,54 @@ __global__ __launch_bounds__(512) void mla_decode_split(DecodeArgs a) {
     float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = xor32_max(xor16_max(mx));
-    float neg;
-    const float alpha = softmax_rescale(st, mx, c, neg);
-    float rs = 0.f;
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_ref * c + 8.f)) {  // lazy rescale (P <= 2^8)
+      const float m_new = fmaxf(m_ref, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast((m_ref - m_use) * c);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < MLA_DV / 16; d++) o[d] *= alpha;
+      m_ref = m_new;
+      neg = -m_use * c;
+    }
+    float e[8];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const float e = exp2_fast(fmaf(s[kb][v], c, neg));
-        s[kb][v] = e;
-        rs += e;
-      }
-    st.l = st.l * alpha + rs;
-    const i32x4_t pb = {pack_bf16(s[0][0], s[0][1]), pack_bf16(s[0][2], s[0][3]), pack_bf16(s[1][0], s[1][1]),
-                        pack_bf16(s[1][2], s[1][3])};
+      for (int v = 0; v < 4; v++) e[4 * kb + v] = exp2_fast(fmaf(s[kb][v], c, neg));
+    const i32x4_t pb = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
+#pragma unroll
+    for (int i = 0; i < 4; i++) l = dot2_bf16(pb[i], kBf16PairOne, l);
 #pragma unroll
     for (int db = 0; db < MLA_DV / 16; db++) {
-      o[db] *= alpha;
-      const int col = 16 * db + 4 * (l16 & 3);
-      i32x2_t part[2];
-#pragma unroll
-      for (int u = 0; u < 2; u++) {
-        const int row = 16 * u + 4 * g + (l16 >> 2);
-        part[u] = lds_tr16(kt + row * MLA_ROWB + ((((uint32_t)col >> 3) ^ swz_half(row)) << 4) + (((col >> 2) & 1) << 3));
-      }
-      o[db] = mfma16x16x32_bf16(cat(part[0], part[1]), pb, o[db]);
+      const uint32_t lc = 2 * db + vc0;
+      const i32x2_t lo = lds_tr16(kt + vrow[0] + (((lc & ~15u) | ((lc & 15u) ^ vsw[0])) << 4));
+      const i32x2_t hi = lds_tr16(kt + vrow[1] + (((lc & ~15u) | ((lc & 15u) ^ vsw[1])) << 4));
+      o[db] = mfma16x16x32_bf16(cat(lo, hi), pb, o[db]);
+      if (db % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  issue(0, st[0]);
+  if (1 < n_tiles) issue(1, st[1]);
+  for (int t = 0; t < n_tiles; t += 3) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= n_tiles) break;
+    tile(std::integral_constant<int, 1>{}, t + 1);
+    if (t + 2 >= n_tiles) break;
+    tile(std::integral_constant<int, 2>{}, t + 2);
   }
 
-  const float l_tot = xor32_sum(xor16_sum(st.l));
-  const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + split;
-  float* po = a.part_o + pidx * MLA_DV;
+  const float l_tot = xor32_sum(xor16_sum(l));
+  if (hvalid) {
+    const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + split;
+    float* po = a.part_o + pidx * MLA_DV;
 #pragma unroll
-  for (int db = 0; db < MLA_DV / 16; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
-  if (g == 0) {
-    a.part_ml[2 * pidx] = st.m;
-    a.part_ml[2 * pidx + 1] = l_tot;
+    for (int db = 0; db < MLA_DV / 16; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
+    if (g == 0) {
+      a.part_ml[2 * pidx] = m_ref;
+      a.part_ml[2 * pidx + 1] = l_tot;
+    }
   }
 }
 
@@ -389,7 +434,7 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_mla_decode(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.n_split, a.B);
-  mla_decode_split<<<grid, 64 * (a.Hq / 16), 0, s>>>(a);
+  mla_decode_split<<<grid, 64 * MLA_NW, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   combine_kernel<<<a.B * a.Hq, 256, 0, s>>>(a, MLA_DV);
