@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < VOPS; i++) {
     const uint32_t row = 4 * i + g;
-    voff[i] = row * rstride + ((l16 ^ swz256(row)) << 4);
+    voff[i] = row * rstride + ((l16 ^ swz16(row)) << 4);
   }
   // transposing V reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4) .. +3.  The column
   // slab of block db is chunk pair db: swizzled to pair db ^ (swz >> 1), chunk (l16%4)/2 of
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
   uint32_t vrow[2], vpair[2];
 #pragma unroll
   for (int u = 0; u < 2; u++) {
-    const uint32_t row = 16 * u + 4 * g + (l16 >> 2), sw = swz256(row);
+    const uint32_t row = 16 * u + 4 * g + (l16 >> 2), sw = swz16(row);
     vrow[u] = row * ROWB + (((((l16 & 3) >> 1) ^ (sw & 1))) << 4) + ((l16 & 1) << 3);
     vpair[u] = sw >> 1;
   }
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < VOPS; i++) {
         const uint32_t row = 4 * i + g, rc = min(row, (uint32_t)(valid - 1));
-        dma16_buf(r, dst + i * 1024, rc * rstride + ((l16 ^ swz256(row)) << 4));
+        dma16_buf(r, dst + i * 1024, rc * rstride + ((l16 ^ swz16(row)) << 4));
       }
     }
   };
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 // room for deep read-ahead: LDS fragments are read in small groups.
 //
 // In LDS a latent row occupies 1280 bytes (five 256-byte bank rows; the last 128 bytes are
-// padding), so every row starts on the same bank and the 4-bit XOR swizzle of 256-byte rows
-// applies within each group of 16 chunks.
+// padding), so every row starts on the same bank and the swz16 XOR pattern of the decode
+// layout applies within each group of 16 chunks.
 
 constexpr int MLA_DK = 576, MLA_DV = 512, MLA_ROWB = 1152, MLA_LROWB = 1280;
 constexpr int MLA_LTILE = TK * MLA_LROWB;             // 40 KiB per stage
@@ -214,7 +214,7 @@ static_assert(MLA_LTILE % (1024 * MLA_NW) == 0, "tile copy split");
 
 // physical 16-byte chunk of logical chunk lc in LDS row `row`
 __device__ __forceinline__ uint32_t mla_chunk(uint32_t row, uint32_t lc) {
-  return (lc & ~15u) | ((lc & 15u) ^ swz256(row));
+  return (lc & ~15u) | ((lc & 15u) ^ swz16(row));
 }
 
 __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
@@ -258,13 +258,13 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
       dma16_buf(r, dst + blk * 1024, rc * MLA_ROWB + lc * 16);
     }
   };
-  const uint32_t ksw = swz256(l16);  // S^T A operand: row 16kb + l16, logical chunk 4cc + g
+  const uint32_t ksw = swz16(l16);  // S^T A operand: row 16kb + l16, logical chunk 4cc + g
   uint32_t vrow[2], vsw[2];         // V^T reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4)
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     const uint32_t row = 16 * u + 4 * g + (l16 >> 2);
     vrow[u] = row * MLA_LROWB + ((l16 & 1) << 3);
-    vsw[u] = swz256(row);
+    vsw[u] = swz16(row);
   }
   const uint32_t vc0 = (l16 & 3) >> 1;  // logical chunk of column block db: 2db + vc0
 

@@ -129,6 +129,12 @@ __device__ __forceinline__ void barrier() {
 __device__ __forceinline__ uint32_t swz256(uint32_t row) {
   return ((row & 3u) << 2) | ((row >> 2) & 3u);
 }
+// The decode kernels' 16x16x32 layout reads V^T with 32 lanes covering 8 consecutive rows
+// of one 32-byte column slab (and K with 16 consecutive rows of one chunk): swz16 makes the
+// chunk-pair index (xor >> 1) equal row % 8 and stays one-to-one over row % 16.
+__device__ __forceinline__ uint32_t swz16(uint32_t row) {
+  return ((row & 7u) << 1) | ((row >> 3) & 1u);
+}
 __device__ __forceinline__ uint32_t swz_half(uint32_t row) {
   uint32_t t = (row >> 1) & 7u;
   return ((t & 1u) << 1) | ((t >> 1) & 1u) | (t & 4u);
