@@ -230,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
   const int end = min(start + a.chunk, L);
   const int n_tiles = (end - start + TK - 1) / TK;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const int wave = wave_id(), lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int h = 16 * wave + l16;
   const bool hvalid = h < a.Hq;
   const float c = a.scale * kLog2e;

@@ -112,6 +112,10 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value: branches on
+// it then stay scalar branches instead of exec-mask regions.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // ------------------------------------------------------------------ LDS swizzles
 //
 // K/V tiles live in LDS as rows of keys, 16-byte chunks XOR-permuted per row.  Readers:

@@ -234,23 +234,27 @@ struct RowAcc {
   float l;              // lane-partial sum of the bf16-rounded P of this lane's keys
 };
 
-template <class QK, int DV, bool CAUSAL, int KPART>
-__device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFrag& q, const typename QK::Lane& ks,
-                                          const uint32_t (&va)[2][DV / 32], const FA_LDS char* stage, int key0,
-                                          bool masked, int qrow, int off, int Skv, float c, int hl, bool has_ks) {
-  constexpr int VROWB = DV * 2;
-  f32x16_t s[BN / 32];
+// S^T of one K tile (all BN/32 key blocks).
+template <class QK>
+__device__ __forceinline__ void tile_scores(f32x16_t (&s)[BN / 32], const typename QK::QFrag& q,
+                                            const typename QK::Lane& ks, const FA_LDS char* kst, int hl, bool has_ks) {
 #pragma unroll
-  for (int kb = 0; kb < BN / 32; kb++) QK::scores(q, ks, stage, kb, hl, s[kb], has_ks);
+  for (int kb = 0; kb < BN / 32; kb++) QK::scores(q, ks, kst, kb, hl, s[kb], has_ks);
+}
+
+// Mask, row max, lazy rescale of O and l, then P^T = exp2(S^T c - m c) packed to bf16 and
+// the row sums of the packed values.
+template <int DV, bool CAUSAL>
+__device__ __forceinline__ void tile_softmax(RowAcc<DV>& st, f32x16_t (&s)[BN / 32], i32x4_t (&pb)[BN / 32][2],
+                                             int key0, bool masked, int qrow, int off, int Skv, float c, int hl) {
   if (masked) {
+    // register v of block kb holds key key0 + 4hl + (32kb + 8(v/4) + v%4): visible iff
+    // that constant offset is below lim
+    const int lim = (CAUSAL ? min(Skv, qrow + off + 1) : Skv) - key0 - 4 * hl;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; kb++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * hl + (v & 3);
-        const bool vis = key < Skv && (!CAUSAL || key <= qrow + off);
-        s[kb][v] = vis ? s[kb][v] : -INFINITY;
-      }
+      for (int v = 0; v < 16; v++) s[kb][v] = (32 * kb + 8 * (v >> 2) + (v & 3)) < lim ? s[kb][v] : -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -268,7 +272,6 @@ __device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFr
     st.m_ref = m_new;
     st.neg = -m_use * c;
   }
-  i32x4_t pb[BN / 32][2];
 #pragma unroll
   for (int kb = 0; kb < BN / 32; kb++)
 #pragma unroll
@@ -280,18 +283,35 @@ __device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFr
 #pragma unroll
       for (int i = 0; i < 4; i++) st.l = dot2_bf16(pb[kb][tp][i], kBf16PairOne, st.l);
     }
-  // O^T += V^T . P^T
+}
+
+// O^T += V^T . P^T over one V tile (rows of DV bf16 at vst).
+template <int DV>
+__device__ __forceinline__ void tile_pv(RowAcc<DV>& st, const i32x4_t (&pb)[BN / 32][2],
+                                        const uint32_t (&va)[2][DV / 32], const FA_LDS char* vst) {
+  constexpr int VROWB = DV * 2;
 #pragma unroll
   for (int kb = 0; kb < BN / 32; kb++)
 #pragma unroll
     for (int tp = 0; tp < 2; tp++)
 #pragma unroll
       for (int db = 0; db < DV / 32; db++) {
-        const int rows = KPART + (32 * kb + 16 * tp) * VROWB;
-        const i32x2_t lo = lds_tr16(stage + va[0][db] + rows);
-        const i32x2_t hi = lds_tr16(stage + va[1][db] + rows);
+        const int rows = (32 * kb + 16 * tp) * VROWB;
+        const i32x2_t lo = lds_tr16(vst + va[0][db] + rows);
+        const i32x2_t hi = lds_tr16(vst + va[1][db] + rows);
         st.o[db] = mfma32x32x16_bf16(cat(lo, hi), pb[kb][tp], st.o[db]);
       }
+}
+
+template <class QK, int DV, bool CAUSAL, int KPART>
+__device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFrag& q, const typename QK::Lane& ks,
+                                          const uint32_t (&va)[2][DV / 32], const FA_LDS char* stage, int key0,
+                                          bool masked, int qrow, int off, int Skv, float c, int hl, bool has_ks) {
+  f32x16_t s[BN / 32];
+  tile_scores<QK>(s, q, ks, stage, hl, has_ks);
+  i32x4_t pb[BN / 32][2];
+  tile_softmax<DV, CAUSAL>(st, s, pb, key0, masked, qrow, off, Skv, c, hl);
+  tile_pv<DV>(st, pb, va, stage + KPART);
 }
 
 // ------------------------------------------------------------------------------------
@@ -308,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qb
   FA_LDS char* stage0 = (FA_LDS char*)stage0_raw;
   FA_LDS char* stage1 = (FA_LDS char*)stage1_raw;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int l32 = lane & 31, hl = lane >> 5;
 
   // work item: contiguous per XCD (workgroup i runs on XCD i % 8), head-major
@@ -413,6 +433,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qb
     }
   }
 }
+
 
 int items(const PrefillArgs& a, int& n_qblocks) {
   n_qblocks = (a.Sq + BM - 1) / BM;

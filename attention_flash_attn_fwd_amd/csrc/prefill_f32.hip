@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs p, int n_q
   constexpr int BNF = 32, LD = D + 4;
   __shared__ float kt[BNF][LD];
   __shared__ float vt[BNF][LD];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int BH = p.B * p.Hq;
   const int rank = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int qb = CAUSAL ? (n_qblocks - 1 - rank) : rank;
