@@ -194,33 +194,38 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// MLA decode split: one workgroup of 8 waves per (split, batch); wave w owns heads
-// 16w .. 16w+15 as the 16 MFMA columns of v_mfma_f32_16x16x32_bf16 (S^T = K.Q^T, then
-// O^T = V^T.P^T).  The 576-wide latent tile (32 keys) is copied into a three-stage LDS ring
-// by direct loads and read by every wave: all 576 columns feed S^T and, through
-// transposing reads, its first 512 columns feed O^T, so the cache is read from HBM once.
-// Q^T (72 VGPRs) and O^T (128) stay in registers at two waves per SIMD, which leaves no
-// room for deep read-ahead: LDS fragments are read in small groups.
+// MLA decode split: one workgroup of 8 waves per (split, batch).  The heads form four
+// groups of 32 -- the N columns of v_mfma_f32_32x32x16_bf16 -- and each group is served by
+// the pair of waves w, w + 4 that share a SIMD.  For S^T = K.Q^T the pair splits the
+// 576-deep contraction: wave half hh = w / 4 takes the 16-column steps 2i + hh, and the two
+// partial S^T meet through LDS (the sum is formed identically by both waves).  For
+// O^T = V^T.P^T the pair splits the 512 output columns (hh selects 256 of them).  So a
+// wave keeps half of Q^T (72 VGPRs) and half of O^T (128), and every 16-byte K read or
+// 8-byte transposed V read feeds a 32x32 product.  The 576-wide latent tile (32 keys) is
+// copied once per workgroup into a three-stage LDS ring by direct loads; its first 512
+// columns are V, so the cache is read from HBM once.
 //
-// In LDS a latent row occupies 1280 bytes (five 256-byte bank rows; the last 128 bytes are
-// padding), so every row starts on the same bank and the swz16 XOR pattern of the decode
-// layout applies within each group of 16 chunks.
+// In LDS a latent row occupies 1280 bytes (1152 used), so every row starts on the same
+// bank; swz256 permutes the 16-byte chunks within each 256-byte group.
 
 constexpr int MLA_DK = 576, MLA_DV = 512, MLA_ROWB = 1152, MLA_LROWB = 1280;
 constexpr int MLA_LTILE = TK * MLA_LROWB;             // 40 KiB per stage
 constexpr int MLA_NW = 8, MLA_NS = 3;
 constexpr int MLA_OPS = MLA_LTILE / 1024 / MLA_NW;    // direct copies per wave per tile
+constexpr int MLA_KS = MLA_DK / 32;                   // contraction steps per wave (18)
+constexpr int MLA_DB = MLA_DV / 64;                   // 32-column output blocks per wave (8)
 static_assert(MLA_LTILE % (1024 * MLA_NW) == 0, "tile copy split");
 
 // physical 16-byte chunk of logical chunk lc in LDS row `row`
 __device__ __forceinline__ uint32_t mla_chunk(uint32_t row, uint32_t lc) {
-  return (lc & ~15u) | ((lc & 15u) ^ swz16(row));
+  return (lc & ~15u) | ((lc & 15u) ^ swz256(row));
 }
 
 __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0_raw[MLA_LTILE];
   __shared__ __attribute__((aligned(1024))) char st1_raw[MLA_LTILE];
   __shared__ __attribute__((aligned(1024))) char st2_raw[MLA_LTILE];
+  __shared__ __attribute__((aligned(1024))) char xs_raw[MLA_NW * 4096];  // partial S^T per wave
   FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw};
 
   const int split = blockIdx.x, b = blockIdx.y;
@@ -230,17 +235,19 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
   const int end = min(start + a.chunk, L);
   const int n_tiles = (end - start + TK - 1) / TK;
 
-  const int wave = wave_id(), lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
-  const int h = 16 * wave + l16;
+  const int wave = wave_id(), lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
+  const int hh = wave >> 2;
+  const int h = 32 * (wave & 3) + l32;
   const bool hvalid = h < a.Hq;
   const float c = a.scale * kLog2e;
 
-  // Q^T as the B operand: column l16 = head h, k = latent column 32cc + 8g .. +7
-  i32x4_t qf[MLA_DK / 32];
+  // Q^T half as the B operand: column l32 = head h; step i covers latent columns
+  // 16 (2i + hh) + 8hl .. +7
+  i32x4_t qf[MLA_KS];
   {
-    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * MLA_ROWB;
+    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * MLA_ROWB + 32 * hh + 16 * hl;
 #pragma unroll
-    for (int cc = 0; cc < MLA_DK / 32; cc++) qf[cc] = *(const i32x4_t*)(qp + cc * 64 + g * 16);
+    for (int i = 0; i < MLA_KS; i++) qf[i] = *(const i32x4_t*)(qp + 64 * i);
   }
   const char* kv = (const char*)a.k + (size_t)b * a.max_len * MLA_ROWB;
   // direct copy of a tile: LDS byte o = blk*1024 + 16*lane is row o / 1280, physical chunk
@@ -258,20 +265,35 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
       dma16_buf(r, dst + blk * 1024, rc * MLA_ROWB + lc * 16);
     }
   };
-  const uint32_t ksw = swz16(l16);  // S^T A operand: row 16kb + l16, logical chunk 4cc + g
-  uint32_t vrow[2], vsw[2];         // V^T reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4)
+  // S^T A operand: key row l32, logical chunk 2(2i + hh) + hl = 4i + 2hh + hl; its XOR part
+  // depends on i % 4 only
+  uint32_t koff[4];
+  {
+    const uint32_t sw = swz256(l32) ^ (2u * hh);
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const uint32_t row = 16 * u + 4 * g + (l16 >> 2);
-    vrow[u] = row * MLA_LROWB + ((l16 & 1) << 3);
-    vsw[u] = swz16(row);
+    for (int q = 0; q < 4; q++) koff[q] = l32 * MLA_LROWB + ((((4u * q + hl) & 15u) ^ sw) << 4);
   }
-  const uint32_t vc0 = (l16 & 3) >> 1;  // logical chunk of column block db: 2db + vc0
+  // V^T reads (A operand of O^T): key rows 16tp + 8u + 4(g/2) + i16/4, output columns
+  // 256hh + 32db + 16(g%2) + 4(i16%4) .. +3; the XOR part depends on u and db % 4
+  uint32_t voff[2][4];
+  {
+    const uint32_t g = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const uint32_t row = 8 * u + 4 * (g >> 1) + (i16 >> 2);
+        const uint32_t lc = 4 * q + 2 * (g & 1) + ((i16 & 3) >> 1);
+        voff[u][q] = row * MLA_LROWB + 512u * hh + ((lc ^ swz256(row)) << 4) + ((i16 & 1) << 3);
+      }
+  }
 
   float m_ref = -INFINITY, neg = 0.f, l = 0.f;
-  f32x4_t o[MLA_DV / 16];
+  f32x16_t o[MLA_DB];
 #pragma unroll
-  for (int d = 0; d < MLA_DV / 16; d++) o[d] = f32x4_t{};
+  for (int d = 0; d < MLA_DB; d++) o[d] = f32x16_t{};
+  FA_LDS char* const xs_own = (FA_LDS char*)xs_raw + wave * 4096 + lane * 16;
+  const FA_LDS char* const xs_peer = (FA_LDS char*)xs_raw + (wave ^ 4) * 4096 + lane * 16;
 
   auto tile = [&](auto SLOT, int t) {
     constexpr int sl = decltype(SLOT)::value;
@@ -282,54 +304,63 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
     barrier();
     if (t + 2 < n_tiles) issue(t + 2, st[(sl + 2) % MLA_NS]);
     const FA_LDS char* kt = st[sl];
-    f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
+    // partial S^T over this wave's half of the contraction
+    f32x16_t s{};
 #pragma unroll
-    for (int cc = 0; cc < MLA_DK / 32; cc++) {
-      const uint32_t lc = 4 * cc + g;
-#pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
-        const i32x4_t ka = lds_b128(kt + (16 * kb + l16) * MLA_LROWB + (((lc & ~15u) | ((lc & 15u) ^ ksw)) << 4));
-        s[kb] = mfma16x16x32_bf16(ka, qf[cc], s[kb]);
-      }
-      if (cc % 3 == 2) __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < MLA_KS; i++) {
+      s = mfma32x32x16_bf16(lds_b128(kt + koff[i & 3] + 256 * (i >> 2)), qf[i], s);
+      if (i % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = 0; j < 4; j++) *(FA_LDS f32x4_t*)(xs_own + 1024 * j) = f32x4_t{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+    barrier();
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f32x4_t pv = lds_f32x4(xs_peer + 1024 * j);
+#pragma unroll
+      for (int v = 0; v < 4; v++) s[4 * j + v] += pv[v];
+    }
+    // register v holds key 8(v/4) + 4hl + v%4 of the tile
     const int key0 = start + t * TK;
     if (key0 + TK > end) {
+      const int lim = end - key0 - 4 * hl;
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int v = 0; v < 4; v++)
-          if (key0 + 16 * kb + 4 * g + v >= end) s[kb][v] = -INFINITY;
+      for (int v = 0; v < 16; v++) s[v] = (8 * (v >> 2) + (v & 3)) < lim ? s[v] : -INFINITY;
     }
-    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mx = xor32_max(xor16_max(mx));
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; v++) mx = fmaxf(mx, s[v]);
+    mx = xor32_max(mx);
     if (__builtin_amdgcn_ballot_w64(mx * c > m_ref * c + 8.f)) {  // lazy rescale (P <= 2^8)
       const float m_new = fmaxf(m_ref, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2_fast((m_ref - m_use) * c);
       l *= alpha;
 #pragma unroll
-      for (int d = 0; d < MLA_DV / 16; d++) o[d] *= alpha;
+      for (int d = 0; d < MLA_DB; d++) o[d] *= alpha;
       m_ref = m_new;
       neg = -m_use * c;
     }
-    float e[8];
+    i32x4_t pb[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
+    for (int tp = 0; tp < 2; tp++) {
+      float e[8];
 #pragma unroll
-      for (int v = 0; v < 4; v++) e[4 * kb + v] = exp2_fast(fmaf(s[kb][v], c, neg));
-    const i32x4_t pb = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
+      for (int i = 0; i < 8; i++) e[i] = exp2_fast(fmaf(s[8 * tp + i], c, neg));
+      pb[tp] = i32x4_t{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
 #pragma unroll
-    for (int i = 0; i < 4; i++) l = dot2_bf16(pb[i], kBf16PairOne, l);
-#pragma unroll
-    for (int db = 0; db < MLA_DV / 16; db++) {
-      const uint32_t lc = 2 * db + vc0;
-      const i32x2_t lo = lds_tr16(kt + vrow[0] + (((lc & ~15u) | ((lc & 15u) ^ vsw[0])) << 4));
-      const i32x2_t hi = lds_tr16(kt + vrow[1] + (((lc & ~15u) | ((lc & 15u) ^ vsw[1])) << 4));
-      o[db] = mfma16x16x32_bf16(cat(lo, hi), pb, o[db]);
-      if (db % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 4; i++) l = dot2_bf16(pb[tp][i], kBf16PairOne, l);
     }
+#pragma unroll
+    for (int tp = 0; tp < 2; tp++)
+#pragma unroll
+      for (int db = 0; db < MLA_DB; db++) {
+        const int imm = 16 * tp * MLA_LROWB + 256 * (db >> 2);
+        const i32x2_t lo = lds_tr16(kt + voff[0][db & 3] + imm);
+        const i32x2_t hi = lds_tr16(kt + voff[1][db & 3] + imm);
+        o[db] = mfma32x32x16_bf16(cat(lo, hi), pb[tp], o[db]);
+        if (db % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
   };
 
   issue(0, st[0]);
@@ -342,13 +373,17 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
     tile(std::integral_constant<int, 2>{}, t + 2);
   }
 
-  const float l_tot = xor32_sum(xor16_sum(l));
+  const float l_tot = xor32_sum(l);
   if (hvalid) {
     const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + split;
-    float* po = a.part_o + pidx * MLA_DV;
+    float* po = a.part_o + pidx * MLA_DV + 256 * hh + 4 * hl;
+    // O^T register v of block db holds output column 256hh + 32db + 8(v/4) + 4hl + v%4
 #pragma unroll
-    for (int db = 0; db < MLA_DV / 16; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
-    if (g == 0) {
+    for (int db = 0; db < MLA_DB; db++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *(f32x4_t*)(po + 32 * db + 8 * j) = f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
+    if (hh == 0 && hl == 0) {
       a.part_ml[2 * pidx] = m_ref;
       a.part_ml[2 * pidx + 1] = l_tot;
     }

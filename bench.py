@@ -206,6 +206,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spinup", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps, so that GPU clocks settle")
     ap.add_argument("--workload", default=BENCH_DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU sample")
@@ -228,6 +230,13 @@ def main():
     step, lens, keep = setup(w)
     flops, byts = algorithmic_work(w, lens)
 
+    # clocks ramp up over the first tens of milliseconds of sustained load: run untimed steps
+    # for a fixed time first, then the requested warmup steps
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < args.spinup:
+        for i in range(4):
+            step(i)
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -280,7 +289,7 @@ def main():
         cfg.update({"sum_kv_len": int(sum(lens)), "len_range": [w.len_lo, w.len_hi]})
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "spinup_s": args.spinup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16"}[w.dtype],
         "data": "synthetic (seeded N(0,1), see workloads/)", "config": cfg, "roofline": roof,
