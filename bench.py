@@ -24,6 +24,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "prefill attn TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "hbm": 8000.0}   # TFLOP/s, GB/s
+# What the HIP events around one call time: the whole call (decode = split kernel + combine).
+KERNELS = {"prefill": "prefill kernel", "mla_prefill": "prefill kernel (MLA policy)",
+           "decode": "gqa_decode_split + combine_kernel (one call)",
+           "mla_decode": "mla_decode_split + combine_kernel (one call)"}
 
 
 def algorithmic_work(w, lens=None):
@@ -57,6 +61,18 @@ def algorithmic_work(w, lens=None):
                       + w.Skv * w.Hr * 2 * w.Dr)
         return (f_fp8, f_bf16), byts
     raise ValueError(w.kind)
+
+
+def source_digest() -> str:
+    """sha256 over the kernel and ABI sources, to tie stored counter readings to a build."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_flash_attn_fwd_amd", "csrc")
+    for n in sorted(os.listdir(csrc)):
+        if n.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, n), "rb") as f:
+                h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 # ------------------------------------------------------------------------------- inputs
@@ -211,7 +227,7 @@ def main():
     ap.add_argument("--workload", default=BENCH_DEFAULT, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU sample")
-    ap.add_argument("--traffic", default=None, help="JSON file with HBM traffic per launch from rocprofv3 counters")
+    ap.add_argument("--traffic", default=None, help="JSON with HBM traffic per launch from rocprofv3 counters (default profiles/traffic.json)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device-to-device copy instead (scales FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -265,20 +281,23 @@ def main():
         value = total / (ms_per_step * 1e-3) / 1e12
         achieved = total / (launch_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
+                "frac": round(achieved / peak, 4), "kernel": KERNELS[w.kind]}
         unit = "TFLOP/s"
     else:
         value = byts / (ms_per_step * 1e-3) / 1e9
         achieved = byts / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm"], "unit": "GB/s",
-                "frac": round(achieved / PEAK["hbm"], 4)}
+                "frac": round(achieved / PEAK["hbm"], 4), "kernel": KERNELS[w.kind]}
         unit = "GB/s"
     traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
+    tpath = args.traffic or os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
             tr = json.load(f)
-        if tr.get("workload") == w.name:
-            traffic = tr.get("bytes_per_launch")
+        rec = tr.get("workloads", {}).get(w.name)
+        # counters describe the kernels they were taken on: ignore them once the sources changed
+        if rec is not None and tr.get("source_sha256") == source_digest():
+            traffic = rec.get("bytes_per_launch")
     roof["traffic"] = traffic
 
     cfg = {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
