@@ -80,6 +80,7 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
   if (!q || !o || !kv_lens || (max_kv_len > 0 && (!k_cache || !v_cache))) return ATTN_ERR_NULL;
   const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);
   if (B > 65535 || p.n_split > 65535 || elems({p.n_split, Hkv, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (elems({B, Hq, D}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
   const size_t need = fa::decode_workspace_bytes(B, Hq, D, p.n_split);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   fa::DecodeArgs a{};
@@ -131,6 +132,7 @@ int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, con
   if (!q || !o || !kv_lens || (max_kv_len > 0 && !kv_cache)) return ATTN_ERR_NULL;
   const fa::SplitPlan p = fa::mla_decode_plan(B, H, max_kv_len);
   if (B > 65535 || elems({p.n_split, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (elems({B, H, Dv}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
   const size_t need = fa::decode_workspace_bytes(B, H, Dv, p.n_split);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   fa::DecodeArgs a{};

@@ -391,32 +391,45 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// Combine: one workgroup per (batch, head); merges the splits that cover [0, L_b) in
-// split order (deterministic, no atomics).
+// Combine: merges, for every (batch, head) row, the splits that cover [0, L_b) in split
+// order (deterministic, no atomics): O = sum_s w_s O_s / sum_s w_s l_s with
+// w_s = exp2((m_s - M) c), M = max_s m_s.  A thread owns 8 consecutive output columns of
+// one row, so its loads of the partials are independent 16-byte reads.
+
+constexpr int CMB_COLS = 8;
 
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
-  const int bh = blockIdx.x, b = bh / a.Hq, h = bh % a.Hq;
+  const int tpr = Dv / CMB_COLS;  // threads per row
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int bh = gid / tpr, d0 = (gid % tpr) * CMB_COLS;
+  if (bh >= a.B * a.Hq) return;
+  const int b = bh / a.Hq;
   const int L = min(max(a.kv_lens[b], 0), a.max_len);
   const int ns = (L + a.chunk - 1) / a.chunk;
   const float c = a.scale * kLog2e;
   const float* ml = a.part_ml + (size_t)bh * a.n_split * 2;
-  const float* po = a.part_o + (size_t)bh * a.n_split * Dv;
+  const float* po = a.part_o + (size_t)bh * a.n_split * Dv + d0;
   float M = -INFINITY;
   for (int s = 0; s < ns; s++) M = fmaxf(M, ml[2 * s]);
   float den = 0.f;
-  for (int s = 0; s < ns; s++) den += exp2_fast((ml[2 * s] - M) * c) * ml[2 * s + 1];
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  __bf16* out = (__bf16*)a.o + (size_t)bh * Dv;
-  for (int d = 2 * threadIdx.x; d < Dv; d += 2 * blockDim.x) {
-    float x0 = 0.f, x1 = 0.f;
-    for (int s = 0; s < ns; s++) {
-      const float w = exp2_fast((ml[2 * s] - M) * c);
-      x0 = fmaf(w, po[(size_t)s * Dv + d], x0);
-      x1 = fmaf(w, po[(size_t)s * Dv + d + 1], x1);
+  f32x4_t x0{}, x1{};
+#pragma unroll 4
+  for (int s = 0; s < ns; s++) {
+    const float w = exp2_fast((ml[2 * s] - M) * c);
+    den = fmaf(w, ml[2 * s + 1], den);
+    const f32x4_t u0 = *(const f32x4_t*)(po + (size_t)s * Dv);
+    const f32x4_t u1 = *(const f32x4_t*)(po + (size_t)s * Dv + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      x0[i] = fmaf(w, u0[i], x0[i]);
+      x1[i] = fmaf(w, u1[i], x1[i]);
     }
-    *(int*)(out + d) = pack_bf16(x0 * inv, x1 * inv);
   }
-  if (a.lse && threadIdx.x == 0) a.lse[bh] = den > 0.f ? M * a.scale + logf(den) : -INFINITY;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  __bf16* out = (__bf16*)a.o + (size_t)bh * Dv + d0;
+  *(i32x4_t*)out = i32x4_t{pack_bf16(x0[0] * inv, x0[1] * inv), pack_bf16(x0[2] * inv, x0[3] * inv),
+                           pack_bf16(x1[0] * inv, x1[1] * inv), pack_bf16(x1[2] * inv, x1[3] * inv)};
+  if (a.lse && d0 == 0) a.lse[bh] = den > 0.f ? M * a.scale + logf(den) : -INFINITY;
 }
 
 }  // namespace
@@ -463,7 +476,7 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<<<a.B * a.Hq, 64, 0, s>>>(a, 128);
+  combine_kernel<<<(a.B * a.Hq * (128 / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, 128);
   return hipGetLastError();
 }
 
@@ -472,7 +485,7 @@ hipError_t launch_mla_decode(const DecodeArgs& a, hipStream_t s) {
   mla_decode_split<<<grid, 64 * MLA_NW, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<<<a.B * a.Hq, 256, 0, s>>>(a, MLA_DV);
+  combine_kernel<<<(a.B * a.Hq * (MLA_DV / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, MLA_DV);
   return hipGetLastError();
 }
 
