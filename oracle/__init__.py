@@ -14,10 +14,14 @@ online-softmax rescale) and the nope/rope + q_scale/k_scale split of MLA; they
 never print the softmax, so the textbook definition stands in for it.  The
 oracle never blocks over keys (that would be the online algorithm it checks).
 
+It also holds the per-token e4m3 quantiser (oracle/quantize.py) that produces the
+MLA prefill nope operands and their fp32 scales.
+
 parity pins: see tests/test_oracle_*.py (brute force, torch CPU fp64 SDPA,
-closed forms, invariants, the OCP e4m3 code table).
+closed forms, invariants, the OCP e4m3 code table, torch float8 casts).
 """
 from .codecs import bf16_to_f64, e4m3_to_f64, E4M3_TABLE
+from .quantize import e4m3_round, quantize_rows, row_scale
 from .attention import (
     sdpa_rows,
     prefill,
@@ -29,6 +33,6 @@ from .attention import (
 )
 
 __all__ = [
-    "bf16_to_f64", "e4m3_to_f64", "E4M3_TABLE",
+    "bf16_to_f64", "e4m3_to_f64", "E4M3_TABLE", "e4m3_round", "quantize_rows", "row_scale",
     "sdpa_rows", "prefill", "prefill_rows", "decode", "mla_prefill", "mla_prefill_rows", "mla_decode",
 ]
