@@ -30,6 +30,7 @@ EXPORTS = {
     "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "mla_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
                        [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "quantize_rows_e4m3": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
 }
 
 _lib = None
@@ -185,3 +186,23 @@ def mla_decode(q, kv_cache, kv_lens, dv: int = 512, scale: float | None = None, 
                               scale, _ptr(workspace), workspace.numel(), _stream())
     _check("mla_decode_fwd", st)
     return (o, lse) if return_lse else o
+
+
+def quantize_rows_e4m3(x, codes=None, scale=None):
+    """Per-row e4m3 quantisation of fp32 x [..., cols]: returns (codes uint8 [..., cols],
+    scale fp32 [...]) with scale = amax/448 per row and codes = e4m3fn(x / scale)."""
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise TypeError("x must be a contiguous fp32 device tensor")
+    if x.dim() < 1:
+        raise ValueError("x needs a last (row) axis")
+    cols = x.shape[-1]
+    n_rows = x.numel() // cols if cols else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
+    scale = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if scale is None else scale
+    if codes.shape != x.shape or scale.shape != x.shape[:-1]:
+        raise ValueError("codes / scale shape mismatch")
+    if codes.dtype not in _FP8 or scale.dtype != torch.float32 or not codes.is_contiguous() or not scale.is_contiguous():
+        raise TypeError("codes must be contiguous uint8 / float8_e4m3fn, scale contiguous fp32")
+    st = lib().quantize_rows_e4m3(_ptr(x), _ptr(codes), _ptr(scale), n_rows, cols, _stream())
+    _check("quantize_rows_e4m3", st)
+    return codes, scale

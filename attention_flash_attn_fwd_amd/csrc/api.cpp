@@ -145,4 +145,17 @@ int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, con
   return hip_status(fa::launch_mla_decode(a, stream));
 }
 
+int quantize_rows_e4m3(const float* x, uint8_t* codes, float* scale, int n_rows, int cols, hipStream_t stream) {
+  if (n_rows < 0 || cols <= 0) return ATTN_ERR_SHAPE;
+  if (elems({n_rows, cols}) < 0) return ATTN_ERR_SHAPE;
+  if (cols % 4 != 0 || cols > 4096) return ATTN_ERR_UNSUPPORTED;
+  if (n_rows == 0) return ATTN_OK;
+  if (!x || !codes || !scale) return ATTN_ERR_NULL;
+  fa::QuantArgs a{};
+  a.x = x; a.codes = codes; a.scale = scale;
+  a.n_rows = n_rows; a.cols = cols;
+  a.lanes_per_row = fa::quantize_lanes_per_row(cols);
+  return hip_status(fa::launch_quantize_rows(a, stream));
+}
+
 }  // extern "C"

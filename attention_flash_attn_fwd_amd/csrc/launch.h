@@ -36,9 +36,19 @@ struct DecodeArgs {
   float scale;
 };
 
+struct QuantArgs {
+  const float* x;       // [n_rows, cols] fp32
+  uint8_t* codes;       // [n_rows, cols] e4m3fn
+  float* scale;         // [n_rows] fp32
+  int n_rows, cols;
+  int lanes_per_row;    // power of two, from quantize_lanes_per_row(cols)
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, hipStream_t s);
+int quantize_lanes_per_row(int cols);
+hipError_t launch_quantize_rows(const QuantArgs& a, hipStream_t s);
 
 // Split plan of the decode kernels (host-only arithmetic, shared with the workspace query).
 struct SplitPlan {

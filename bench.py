@@ -27,7 +27,8 @@ PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "hbm": 8000.0}   # TFLOP/s,
 # What the HIP events around one call time: the whole call (decode = split kernel + combine).
 KERNELS = {"prefill": "prefill kernel", "mla_prefill": "prefill kernel (MLA policy)",
            "decode": "gqa_decode_split + combine_kernel (one call)",
-           "mla_decode": "mla_decode_split + combine_kernel (one call)"}
+           "mla_decode": "mla_decode_split + combine_kernel (one call)",
+           "quantize": "quantize_rows_kernel"}
 
 
 def algorithmic_work(w, lens=None):
@@ -60,6 +61,9 @@ def algorithmic_work(w, lens=None):
         byts = w.B * (w.Sq * w.Hq * (w.Dn + 2 * w.Dr + 2 * w.Dv + 4) + w.Skv * w.Hq * (w.Dn + 2 * w.Dv + 4)
                       + w.Skv * w.Hr * 2 * w.Dr)
         return (f_fp8, f_bf16), byts
+    if w.kind == "quantize":
+        rows = w.B * w.Sq * w.Hq
+        return 0, rows * (w.Dn * 4 + w.Dn + 4)        # fp32 rows in, e4m3 codes + fp32 scale out
     raise ValueError(w.kind)
 
 
@@ -121,6 +125,12 @@ def setup(w):
         o = torch.empty((w.B, w.Sq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda")
         return (lambda i: fa.mla_prefill(t["q_nope"], t["q_rope"], t["k_nope"], t["k_rope"], t["v"], t["q_scale"],
                                          t["k_scale"], causal=w.causal, scale=w.scale, out=o)), None, (t, o)
+    if w.kind == "quantize":
+        from workloads import make_quantize
+        x = torch.from_numpy(make_quantize(w)["x"]).cuda()
+        codes = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+        scale = torch.empty(x.shape[:-1], dtype=torch.float32, device="cuda")
+        return (lambda i: fa.quantize_rows_e4m3(x, codes, scale)), None, (x, codes, scale)
     raise ValueError(w.kind)
 
 
@@ -170,6 +180,18 @@ def cpu_baseline(w, lens, budget_s: float):
         what = f"{n} (batch, head) pairs x all {w.Sq} query rows"
         return {"value": done_work / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                 "sample": what, "seconds": round(t_used, 2)}
+    if w.kind == "quantize":
+        from workloads import make_quantize
+        d = make_quantize(w, tokens=min(w.Sq, 256))["x"]
+        n = 0
+        while t_used < budget_s and n < 64:
+            t0 = time.perf_counter()
+            oracle.quantize_rows(d)
+            t_used += time.perf_counter() - t0
+            n += 1
+        rows = n * d.shape[0] * d.shape[1] * d.shape[2]
+        return {"value": rows * (w.Dn * 5 + 4) / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{n} passes over the first {d.shape[1]} tokens x {w.Hq} heads rows", "seconds": round(t_used, 2)}
     # decode: whole sequences
     sel = []
     for b in range(w.B):
@@ -283,7 +305,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "kernel": KERNELS[w.kind]}
         unit = "TFLOP/s"
-    else:
+    else:  # decode and quantisation: HBM-bound
         value = byts / (ms_per_step * 1e-3) / 1e9
         achieved = byts / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm"], "unit": "GB/s",
@@ -310,7 +332,7 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "spinup_s": args.spinup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16"}[w.dtype],
+        "dtype": "f32->e4m3" if w.kind == "quantize" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16"}[w.dtype],
         "data": "synthetic (seeded N(0,1), see workloads/)", "config": cfg, "roofline": roof,
         "kernel_ms": round(launch_ms, 4), "algorithmic": {"flops": flops if not isinstance(flops, tuple) else list(flops),
                                                           "bytes": byts},

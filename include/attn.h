@@ -127,6 +127,22 @@ int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse,
                    float softmax_scale, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 
+/*
+ * Per-token e4m3 quantisation: produces the nope operands and scales that
+ * mla_prefill_fwd consumes (MLASmemStorage page: one fp32 scale per Q-tile row,
+ * q_scale_smem, and per K-tile row, k_scale_smem, beside the fp8 nope tiles).
+ * For each of n_rows rows of cols fp32 values:
+ *   scale[r]    = fp32(max_j |x[r][j]| / 448)   (1.0 for an all-zero row)
+ *   codes[r][j] = e4m3fn(fp32(x[r][j] / scale[r])), round to nearest even
+ * (OCP e4m3fn: bias 7, 3 mantissa bits, max 448, no infinity.)
+ *   x: device fp32 [n_rows, cols]; codes: device uint8 [n_rows, cols];
+ *   scale: device fp32 [n_rows]; all contiguous, owned by the caller.
+ *   Rows must be finite; a row holding inf or NaN gives unspecified codes and scale.
+ *   Supported: cols % 4 == 0 and 4 <= cols <= 4096 (else ATTN_ERR_UNSUPPORTED).
+ */
+int quantize_rows_e4m3(const float* x, uint8_t* codes, float* scale, int n_rows, int cols,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,3 +130,15 @@ def test_mla_decode_validation(lib):
     assert mla_decode(lib, kv=NUL) == ENULL
     assert mla_decode(lib, wsb=need - 1) == EWS
     assert mla_decode(lib, B=0, q=NUL, kv=NUL, o=NUL, lens=NUL, ws=NUL) == OK
+
+
+def test_quantize_validation(lib):
+    q = lambda x=FAKE, c=FAKE, s=FAKE, n=4, cols=128: lib.quantize_rows_e4m3(x, c, s, n, cols, S)
+    assert q(n=-1) == ESHAPE
+    assert q(cols=0) == ESHAPE
+    assert q(cols=130) == EUNSUP       # not a multiple of 4
+    assert q(cols=4100) == EUNSUP      # above 4096
+    assert q(n=0) == OK                # empty: nothing to do, no HIP call
+    assert q(x=NUL) == ENULL
+    assert q(c=NUL) == ENULL
+    assert q(s=NUL) == ENULL

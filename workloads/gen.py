@@ -155,3 +155,13 @@ def make_mla_prefill(w: Workload, batches=None) -> dict:
     _fill(w.seed, T_V, bs, w.Skv, (H, Dv), lambda x: (bf16_bits(x),), [v])
     return {"q_nope": qn, "k_nope": kn, "q_scale": qs, "k_scale": ks,
             "q_rope": qr, "k_rope": kr, "v": v, "batches": bs}
+
+
+def make_quantize(w: Workload, batches=None, tokens=None) -> dict:
+    """fp32 rows to quantise: the q_nope draws of the MLA prefill stream of the same seed,
+    x [nb, S, H, Dn] (tokens [0, tokens) only when given)."""
+    bs = _batches(w, batches)
+    S = w.Sq if tokens is None else int(tokens)
+    x = np.zeros((len(bs), S, w.Hq, w.Dn), np.float32)
+    _fill(w.seed, T_QNOPE, bs, S, (w.Hq, w.Dn), lambda v: (v,), [x])
+    return {"x": x, "batches": bs}

@@ -1,4 +1,4 @@
-"""The five synthetic workloads of the forward-attention path, by name.
+"""The synthetic workloads of the forward-attention path, by name.
 
 Each one is a shape, a storage dtype and a seed; the tensors are drawn by
 :mod:`workloads.gen`.  Layouts are token-major and row-major throughout:
@@ -12,7 +12,7 @@ from dataclasses import dataclass, replace
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "decode" | "mla_prefill" | "mla_decode"
+    kind: str                 # "prefill" | "decode" | "mla_prefill" | "mla_decode" | "quantize"
     seed: int
     dtype: str                # storage dtype of q/k/v: "f32" | "bf16" | "fp8+bf16"
     B: int
@@ -62,6 +62,11 @@ WORKLOADS = {
         name="mla_prefill_fp8_causal_b1_h128_s8192", kind="mla_prefill", seed=5, dtype="fp8+bf16",
         B=1, Hq=128, Hkv=128, Sq=8192, Skv=8192, D=192, Dv=128, causal=True, Dn=128, Dr=64, Hr=1,
         scale=1.0 / 192 ** 0.5),
+    # Per-token e4m3 quantisation of the MLA prefill q_nope originals: 8192 tokens x 128 heads
+    # rows of 128 fp32 values (the same draws the MLA prefill workload quantises).
+    "quantize_e4m3_rows_b1_s8192_h128_d128": Workload(
+        name="quantize_e4m3_rows_b1_s8192_h128_d128", kind="quantize", seed=5, dtype="f32",
+        B=1, Hq=128, Hkv=128, Sq=8192, Skv=8192, D=128, Dv=128, Dn=128),
 }
 
 # The workload the benchmark times by default.
