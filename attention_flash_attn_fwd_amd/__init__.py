@@ -23,7 +23,7 @@ EXPORTS = {
     "attn_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 8 +
                          [ctypes.c_float, ctypes.c_void_p]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
-    "attn_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 +
+    "attn_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10 +
                         [ctypes.c_float, ctypes.c_void_p]),
@@ -112,10 +112,22 @@ def decode_workspace_size(B: int, Hq: int, D: int, max_kv_len: int) -> int:
 
 
 def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=None, out=None,
-           return_lse: bool = False):
-    """Decode: q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D] bf16, kv_lens int32 [B] (device) -> o [B,Hq,D]."""
-    _need(q, "q", (torch.bfloat16,), 3); _need(k_cache, "k_cache", (torch.bfloat16,), 4)
-    _need(v_cache, "v_cache", (torch.bfloat16,), 4); _need(kv_lens, "kv_lens", (torch.int32,), 1)
+           return_lse: bool = False, k_scale=None, v_scale=None):
+    """Decode: q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D], kv_lens int32 [B] (device) -> o [B,Hq,D] bf16.
+
+    Caches are bf16, or e4m3 codes (uint8 / float8_e4m3fn) with per-token fp32 scales
+    k_scale, v_scale [B,Lmax,Hkv]."""
+    _need(q, "q", (torch.bfloat16,), 3); _need(kv_lens, "kv_lens", (torch.int32,), 1)
+    fp8 = k_cache.dtype in _FP8
+    if fp8:
+        _need(k_cache, "k_cache", _FP8, 4); _need(v_cache, "v_cache", _FP8, 4)
+        _need(k_scale, "k_scale", (torch.float32,), 3); _need(v_scale, "v_scale", (torch.float32,), 3)
+        if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_cache.shape[:3]:
+            raise ValueError("k_scale / v_scale must be [B, Lmax, Hkv]")
+    else:
+        _need(k_cache, "k_cache", (torch.bfloat16,), 4); _need(v_cache, "v_cache", (torch.bfloat16,), 4)
+        if k_scale is not None or v_scale is not None:
+            raise ValueError("k_scale / v_scale go with e4m3 caches only")
     B, Hq, D = q.shape
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
     if k_cache.shape[0] != B or k_cache.shape[3] != D or v_cache.shape != k_cache.shape or kv_lens.shape[0] != B:
@@ -126,7 +138,8 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=N
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
-    st = lib().attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(kv_lens), ATTN_BF16,
+    st = lib().attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(kv_lens),
+                               _ptr(k_scale), _ptr(v_scale), ATTN_FP8_E4M3 if fp8 else ATTN_BF16,
                                B, Hq, Hkv, D, Lmax, scale, _ptr(workspace), workspace.numel(), _stream())
     _check("attn_decode_fwd", st)
     return (o, lse) if return_lse else o

@@ -69,15 +69,19 @@ size_t attn_decode_workspace_size(int B, int Hq, int D, int max_kv_len) {
 }
 
 int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                    const int32_t* kv_lens, int dtype, int B, int Hq, int Hkv, int D, int max_kv_len,
-                    float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+                    const int32_t* kv_lens, const float* k_scale, const float* v_scale, int dtype, int B,
+                    int Hq, int Hkv, int D, int max_kv_len, float softmax_scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
+  const bool fp8 = dtype == ATTN_FP8_E4M3;
+  if (!fp8 && (k_scale || v_scale)) return ATTN_ERR_DTYPE;  // scales belong to e4m3 caches only
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (elems({B, max_kv_len, Hkv, D}) < 0 || elems({B, Hq, D}) < 0) return ATTN_ERR_SHAPE;
   if (D != 128 || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
   if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
   if (B == 0) return ATTN_OK;
   if (!q || !o || !kv_lens || (max_kv_len > 0 && (!k_cache || !v_cache))) return ATTN_ERR_NULL;
+  if (fp8 && max_kv_len > 0 && (!k_scale || !v_scale)) return ATTN_ERR_NULL;
   const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);
   if (B > 65535 || p.n_split > 65535 || elems({p.n_split, Hkv, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
   if (elems({B, Hq, D}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
@@ -85,12 +89,13 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   fa::DecodeArgs a{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_lens = kv_lens;
+  a.k_scale = k_scale; a.v_scale = v_scale;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + ((size_t)B * Hq * p.n_split * D * 4 + 255) / 256 * 256);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_kv_len;
   a.n_split = p.n_split; a.chunk = p.chunk;
   a.scale = softmax_scale;
-  return hip_status(fa::launch_gqa_decode(a, stream));
+  return hip_status(fa::launch_gqa_decode(a, fp8, stream));
 }
 
 int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope, const void* k_rope, const void* v,
@@ -142,7 +147,7 @@ int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, con
   a.B = B; a.Hq = H; a.Hkv = 1; a.max_len = max_kv_len;
   a.n_split = p.n_split; a.chunk = p.chunk;
   a.scale = softmax_scale;
-  return hip_status(fa::launch_mla_decode(a, stream));
+  return hip_status(fa::launch_mla_decode(a, false, stream));
 }
 
 int quantize_rows_e4m3(const float* x, uint8_t* codes, float* scale, int n_rows, int cols, hipStream_t stream) {

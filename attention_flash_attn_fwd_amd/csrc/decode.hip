@@ -194,6 +194,205 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// GQA decode split over an e4m3 cache with per-token scales (k_scale, v_scale per key row
+// and kv head).  Same structure as the bf16 kernel, at half the bytes per key:
+//  * K (128-byte rows) goes straight into registers; the contraction order is permuted so
+//    that a lane's four K fragments are one contiguous 32-byte run of its key row (step cc,
+//    lane group g, element i covers head dim 32g + 8cc + i; Q^T uses the same order), and
+//    e4m3 -> bf16 is exact, so S^T = K_code.Q^T runs on the bf16 matrix cores and the key
+//    scale multiplies S afterwards;
+//  * V codes are staged in LDS by direct loads with the key and value scales of the tile,
+//    read transposed one byte wide (ds_read_b64_tr_b8: 8 keys of one column per lane, one
+//    read per product instead of two), converted exactly, and the value scale is folded
+//    into P: O += (P . v_scale) V_code.
+
+template <int G>
+__global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
+  constexpr int D = 128, ROWB = 128, VT = TK * ROWB;
+  constexpr int SCB = 256;                         // one scale DMA: 64 lanes x 4 bytes
+  constexpr int STAGE = VT + 2 * SCB;              // V codes | k_scale | v_scale
+  constexpr int KOPS = 4, VOPS = VT / 1024 + 2;    // vector-memory instructions per tile
+  __shared__ __attribute__((aligned(1024))) char v0_raw[STAGE];
+  __shared__ __attribute__((aligned(1024))) char v1_raw[STAGE];
+  FA_LDS char* const vst[2] = {(FA_LDS char*)v0_raw, (FA_LDS char*)v1_raw};
+
+  const int kvh = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  const int L = min(max(a.kv_lens[b], 0), a.max_len);
+  const int start = split * a.chunk;
+  if (start >= L) return;
+  const int end = min(start + a.chunk, L);
+  const int n_tiles = (end - start + TK - 1) / TK;
+
+  const int lane = threadIdx.x, l16 = lane & 15, g = lane >> 4;
+  const float c = a.scale * kLog2e;
+  const uint32_t rstride = (uint32_t)a.Hkv * ROWB;  // bytes between consecutive keys
+  const uint32_t sstride = (uint32_t)a.Hkv * 4;     // scale bytes between consecutive keys
+
+  // Q^T as the B operand: column l16 = query head kvh*G + l16 (zero past the group); step cc
+  // holds head dims 32g + 8cc .. +7
+  i32x4_t qf[D / 32];
+  {
+    const int hq = kvh * G + (l16 < G ? l16 : 0);
+    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + hq) * (D * 2);
+#pragma unroll
+    for (int cc = 0; cc < D / 32; cc++) {
+      const i32x4_t x = *(const i32x4_t*)(qp + (32 * g + 8 * cc) * 2);
+      qf[cc] = l16 < G ? x : i32x4_t{};
+    }
+  }
+  const size_t row0 = (size_t)b * a.max_len * a.Hkv + kvh;  // (batch, key 0, kv head) row index
+  const char* kbase = (const char*)a.k + row0 * ROWB;
+  const char* vbase = (const char*)a.v + row0 * ROWB;
+  const float* ksbase = a.k_scale + row0;
+  const float* vsbase = a.v_scale + row0;
+  // K: key rows 16kb + l16, bytes 32g .. 32g + 31 as two 16-byte loads
+  const uint32_t koff0 = l16 * rstride + 32 * g, koff1 = (16 + l16) * rstride + 32 * g;
+  // V copy: LDS row 8i + lane/8 holds key row 8i + lane/8 with its 16-byte chunks
+  // XOR-permuted by swz_fp8v
+  uint32_t voff[VT / 1024];
+#pragma unroll
+  for (int i = 0; i < VT / 1024; i++) {
+    const uint32_t row = 8 * i + lane / 8;
+    voff[i] = row * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4);
+  }
+  // transposing V reads: lane 2e + h of group g reads key row R = 16(e/4) + 4g + e%4 at
+  // byte 8h of column chunk db, so output byte e of lane l is column 16db + l%16 of key R --
+  // the key order in which P^T is packed below
+  uint32_t vrd, vsw;
+  {
+    const uint32_t e = (lane & 15) >> 1, h = lane & 1;
+    const uint32_t row = 16 * (e >> 2) + 4 * g + (e & 3);
+    vrd = row * ROWB + 8 * h;
+    vsw = swz_fp8v(row);
+  }
+
+  i32x4_t kf[2][2][2];  // [slot][kb][16-byte half]: 32 e4m3 K codes per key row
+  auto issue_k = [&](int t, i32x4_t (&dst)[2][2]) {
+    const int key0 = start + t * TK;
+    const auto r = make_rsrc(kbase + (size_t)key0 * rstride, (uint32_t)(end - key0) * rstride);
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+      dst[0][hh] = __builtin_amdgcn_raw_buffer_load_b128(r, koff0 + 16 * hh, 0, 0);
+      dst[1][hh] = __builtin_amdgcn_raw_buffer_load_b128(r, koff1 + 16 * hh, 0, 0);
+    }
+  };
+  auto issue_v = [&](int t, FA_LDS char* dst) {
+    const int key0 = start + t * TK, valid = min(TK, end - key0);
+    const auto r = make_rsrc(vbase + (size_t)key0 * rstride, (uint32_t)(valid - 1) * rstride + ROWB);
+    if (valid == TK) {
+#pragma unroll
+      for (int i = 0; i < VT / 1024; i++) dma16_buf(r, dst + i * 1024, voff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < VT / 1024; i++) {
+        const uint32_t row = 8 * i + lane / 8, rc = min(row, (uint32_t)(valid - 1));
+        dma16_buf(r, dst + i * 1024, rc * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4));
+      }
+    }
+    // scales of keys key0 + lane (lanes past the tile repeat its last key)
+    const uint32_t so = (uint32_t)min(lane, valid - 1) * sstride;
+    const uint32_t sbytes = (uint32_t)(valid - 1) * sstride + 4;
+    dma4_buf(make_rsrc(ksbase + (size_t)key0 * a.Hkv, sbytes), dst + VT, so);
+    dma4_buf(make_rsrc(vsbase + (size_t)key0 * a.Hkv, sbytes), dst + VT + SCB, so);
+  };
+
+  float m_ref = -INFINITY, neg = 0.f, l = 0.f;
+  f32x4_t o[D / 16];
+#pragma unroll
+  for (int d = 0; d < D / 16; d++) o[d] = f32x4_t{};
+
+  // tile t: K(t) in kf[t & 1] (issued two tiles earlier), V(t) and its scales in
+  // vst[t & 1] (one tile earlier).  Issue order per tile: V(t+1), then K(t+2).
+  auto tile = [&](auto SLOT, int t) {
+    constexpr int sl = decltype(SLOT)::value;
+    if (t + 1 < n_tiles) issue_v(t + 1, vst[sl ^ 1]);
+    f32x4_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+      s[kb] = f32x4_t{};
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++) {
+        const i32x4_t w = kf[sl][kb][hh];
+        s[kb] = mfma16x16x32_bf16(e4m3x8_to_bf16(i32x2_t{w.x, w.y}), qf[2 * hh], s[kb]);
+        s[kb] = mfma16x16x32_bf16(e4m3x8_to_bf16(i32x2_t{w.z, w.w}), qf[2 * hh + 1], s[kb]);
+      }
+    }
+    if (t + 2 < n_tiles) issue_k(t + 2, kf[sl]);
+    // V(t) and the scales of tile t must have landed: later vector-memory ops are K(t+1),
+    // V(t+1) with its scales, K(t+2)
+    if (t + 2 < n_tiles) wait_vmcnt<2 * KOPS + VOPS>();
+    else if (t + 1 < n_tiles) wait_vmcnt<KOPS + VOPS>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    const FA_LDS char* vt = vst[sl];
+    // register v of block kb holds key 16kb + 4g + v
+    const f32x4_t ks0 = lds_f32x4(vt + VT + 16 * g), ks1 = lds_f32x4(vt + VT + 64 + 16 * g);
+    const f32x4_t vs0 = lds_f32x4(vt + VT + SCB + 16 * g), vs1 = lds_f32x4(vt + VT + SCB + 64 + 16 * g);
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      s[0][v] *= ks0[v];
+      s[1][v] *= ks1[v];
+    }
+    const int key0 = start + t * TK;
+    if (key0 + TK > end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+          if (key0 + 16 * kb + 4 * g + v >= end) s[kb][v] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = xor32_max(xor16_max(mx));
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_ref * c + 8.f)) {  // lazy rescale (P <= 2^8)
+      const float m_new = fmaxf(m_ref, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast((m_ref - m_use) * c);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < D / 16; d++) o[d] *= alpha;
+      m_ref = m_new;
+      neg = -m_use * c;
+    }
+    float e[8];
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        e[4 * kb + v] = exp2_fast(fmaf(s[kb][v], c, neg));
+        l += e[4 * kb + v];
+      }
+    const i32x4_t pb = {pack_bf16(e[0] * vs0[0], e[1] * vs0[1]), pack_bf16(e[2] * vs0[2], e[3] * vs0[3]),
+                        pack_bf16(e[4] * vs1[0], e[5] * vs1[1]), pack_bf16(e[6] * vs1[2], e[7] * vs1[3])};
+#pragma unroll
+    for (int db = 0; db < D / 16; db++)
+      o[db] = mfma16x16x32_bf16(e4m3x8_to_bf16(lds_tr8(vt + vrd + ((db ^ vsw) << 4))), pb, o[db]);
+  };
+
+  issue_k(0, kf[0]);
+  issue_v(0, vst[0]);
+  if (1 < n_tiles) issue_k(1, kf[1]);
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= n_tiles) break;
+    tile(std::integral_constant<int, 1>{}, t + 1);
+  }
+
+  const float l_tot = xor32_sum(xor16_sum(l));
+  if (l16 < G) {
+    const int hq = kvh * G + l16;
+    const size_t pidx = ((size_t)b * a.Hq + hq) * a.n_split + split;
+    float* po = a.part_o + pidx * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
+    if (g == 0) {
+      a.part_ml[2 * pidx] = m_ref;
+      a.part_ml[2 * pidx + 1] = l_tot;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // MLA decode split: one workgroup of 8 waves per (split, batch).  The heads form four
 // groups of 32 -- the N columns of v_mfma_f32_32x32x16_bf16 -- and each group is served by
 // the pair of waves w, w + 4 that share a SIMD.  For S^T = K.Q^T the pair splits the
@@ -464,11 +663,15 @@ size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split) {
   return o_bytes + rows * 2 * 4;
 }
 
-hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_gqa_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   dim3 grid(a.Hkv, a.n_split, a.B);
   switch (G) {
-#define FA_G(n) case n: gqa_decode_split<n><<<grid, 64, 0, s>>>(a); break;
+#define FA_G(n)                                                   \
+  case n:                                                         \
+    if (fp8) gqa_decode_split_fp8<n><<<grid, 64, 0, s>>>(a);      \
+    else gqa_decode_split<n><<<grid, 64, 0, s>>>(a);              \
+    break;
     FA_G(1) FA_G(2) FA_G(3) FA_G(4) FA_G(5) FA_G(6) FA_G(7) FA_G(8)
     FA_G(9) FA_G(10) FA_G(11) FA_G(12) FA_G(13) FA_G(14) FA_G(15) FA_G(16)
 #undef FA_G
@@ -480,7 +683,8 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_mla_decode(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
+  if (fp8) return hipErrorInvalidValue;
   dim3 grid(a.n_split, a.B);
   mla_decode_split<<<grid, 64 * MLA_NW, 0, s>>>(a);
   hipError_t e = hipGetLastError();

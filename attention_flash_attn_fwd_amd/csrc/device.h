@@ -69,6 +69,13 @@ __device__ __forceinline__ i32x2_t lds_tr16(const FA_LDS char* p) {
   i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4_t*)p);
   return __builtin_bit_cast(i32x2_t, v);
 }
+// ds_read_b64_tr_b8: within each 16-lane group, lane 8h + b receives byte b of the 8-byte
+// words read by lanes h, h + 2, ..., h + 14 -- i.e. when lanes 2e + h address row e
+// (8 consecutive bytes at column 8h), lane i receives column i of rows 0..7 (measured on
+// gfx950 with a single-wave probe).
+__device__ __forceinline__ i32x2_t lds_tr8(const FA_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2_t*)p);
+}
 __device__ __forceinline__ i32x4_t cat(i32x2_t a, i32x2_t b) {
   i32x4_t r;
   r.x = a.x; r.y = a.y; r.z = b.x; r.w = b.y;
@@ -139,6 +146,12 @@ __device__ __forceinline__ uint32_t swz256(uint32_t row) {
 __device__ __forceinline__ uint32_t swz16(uint32_t row) {
   return ((row & 7u) << 1) | ((row >> 3) & 1u);
 }
+// fp8 V tiles (128-byte rows, two rows per 256-byte bank row): the transposing reads of the
+// decode layout gather 16 rows of one 16-byte column chunk per half-wave; this XOR of the
+// chunk index is one-to-one over each parity class of those rows.
+__device__ __forceinline__ uint32_t swz_fp8v(uint32_t row) {
+  return ((row >> 1) & 3u) | ((row >> 2) & 4u);
+}
 __device__ __forceinline__ uint32_t swz_half(uint32_t row) {
   uint32_t t = (row >> 1) & 7u;
   return ((t & 1u) << 1) | ((t >> 1) & 1u) | (t & 4u);
@@ -180,6 +193,17 @@ __device__ __forceinline__ float dot2_bf16(int a, int b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 constexpr int kBf16PairOne = 0x3F803F80;  // packed bf16 {1.0, 1.0}
+
+// eight e4m3fn codes (bytes of w, low byte first) -> eight bf16, exactly (every e4m3fn value
+// is a bf16 value; v_cvt_scalef32_pk_bf16_fp8 with scale 1, OCP e4m3fn on gfx950)
+__device__ __forceinline__ i32x4_t e4m3x8_to_bf16(i32x2_t w) {
+  i32x4_t r;
+  r.x = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w.x, 1.f, false));
+  r.y = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w.x, 1.f, true));
+  r.z = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w.y, 1.f, false));
+  r.w = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)w.y, 1.f, true));
+  return r;
+}
 
 // two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ int pack_bf16(float a, float b) {

@@ -47,7 +47,10 @@ def algorithmic_work(w, lens=None):
     if w.kind == "decode":
         sl = int(sum(lens))
         flops = 2 * w.Hq * (w.D + w.Dv) * sl
-        byts = sl * w.Hkv * (w.D + w.Dv) * 2 + w.B * w.Hq * (w.D + w.Dv) * 2
+        if w.dtype == "fp8":   # e4m3 K and V rows plus their two fp32 per-token scales
+            byts = sl * w.Hkv * (w.D + w.Dv + 8) + w.B * w.Hq * (w.D + w.Dv) * 2
+        else:
+            byts = sl * w.Hkv * (w.D + w.Dv) * 2 + w.B * w.Hq * (w.D + w.Dv) * 2
         return flops, byts
     if w.kind == "mla_decode":
         sl = int(sum(lens))
@@ -103,9 +106,13 @@ def setup(w):
     if w.kind == "decode":
         d = make_decode(w)
         q, kv_lens = bf16(d["q"]), torch.from_numpy(d["kv_lens"]).cuda()
-        caches = [(bf16(d["k"]), bf16(d["v"]))]
         ws = torch.empty(fa.decode_workspace_size(w.B, w.Hq, w.D, w.Skv), dtype=torch.uint8, device="cuda")
         o = torch.empty_like(q)
+        if w.dtype == "fp8":
+            k, v, ks, vs = (torch.from_numpy(d[n]).cuda() for n in ("k", "v", "k_scale", "v_scale"))
+            return (lambda i: fa.decode(q, k, v, kv_lens, scale=w.scale, workspace=ws, out=o, k_scale=ks,
+                                        v_scale=vs)), d["kv_lens"], (q, k, v, ks, vs, ws, o)
+        caches = [(bf16(d["k"]), bf16(d["v"]))]
         return (lambda i: fa.decode(q, caches[0][0], caches[0][1], kv_lens, scale=w.scale, workspace=ws, out=o)), \
             d["kv_lens"], (q, caches, ws, o)
     if w.kind == "mla_decode":
@@ -192,20 +199,30 @@ def cpu_baseline(w, lens, budget_s: float):
         rows = n * d.shape[0] * d.shape[1] * d.shape[2]
         return {"value": rows * (w.Dn * 5 + 4) / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
                 "sample": f"{n} passes over the first {d.shape[1]} tokens x {w.Hq} heads rows", "seconds": round(t_used, 2)}
-    # decode: whole sequences
+    # decode: whole sequences (drawing and decoding the inputs is not timed; the oracle call is)
     sel = []
     for b in range(w.B):
-        t0 = time.perf_counter()
-        if w.kind == "decode":
+        if w.kind == "decode" and w.dtype == "fp8":
             d = make_decode(w, batches=[b], lens=lens)
             L = int(d["kv_lens"][0])
-            oracle.decode(oracle.bf16_to_f64(d["q"]), oracle.bf16_to_f64(d["k"][:, :L]),
-                          oracle.bf16_to_f64(d["v"][:, :L]), d["kv_lens"], w.scale)
+            args = (oracle.bf16_to_f64(d["q"]),
+                    oracle.e4m3_to_f64(d["k"][:, :L]) * d["k_scale"][:, :L, :, None].astype(np.float64),
+                    oracle.e4m3_to_f64(d["v"][:, :L]) * d["v_scale"][:, :L, :, None].astype(np.float64),
+                    d["kv_lens"], w.scale)
+            fn = oracle.decode
+        elif w.kind == "decode":
+            d = make_decode(w, batches=[b], lens=lens)
+            L = int(d["kv_lens"][0])
+            args = (oracle.bf16_to_f64(d["q"]), oracle.bf16_to_f64(d["k"][:, :L]), oracle.bf16_to_f64(d["v"][:, :L]),
+                    d["kv_lens"], w.scale)
+            fn = oracle.decode
         else:
             d = make_mla_decode(w, batches=[b], lens=lens)
             L = int(d["kv_lens"][0])
-            oracle.mla_decode(oracle.bf16_to_f64(d["q"]), oracle.bf16_to_f64(d["kv"][:, :L]), d["kv_lens"], w.Dv,
-                              w.scale)
+            args = (oracle.bf16_to_f64(d["q"]), oracle.bf16_to_f64(d["kv"][:, :L]), d["kv_lens"], w.Dv, w.scale)
+            fn = oracle.mla_decode
+        t0 = time.perf_counter()
+        fn(*args)
         t_used += time.perf_counter() - t0
         sel.append(L)
         if t_used >= budget_s:
@@ -332,7 +349,8 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "spinup_s": args.spinup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32->e4m3" if w.kind == "quantize" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16"}[w.dtype],
+        "dtype": "f32->e4m3" if w.kind == "quantize" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16",
+                                                           "fp8": "e4m3 cache, bf16 q/o"}[w.dtype],
         "data": "synthetic (seeded N(0,1), see workloads/)", "config": cfg, "roofline": roof,
         "kernel_ms": round(launch_ms, 4), "algorithmic": {"flops": flops if not isinstance(flops, tuple) else list(flops),
                                                           "bytes": byts},

@@ -79,19 +79,25 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
 /*
  * Decode (token generation; AMD buffers page, token_gen variant of the K/V buffers):
  * one query token per sequence attends to keys [0, kv_lens[b]) of its cache.
- *   q [B,Hq,D] bf16; k_cache, v_cache [B,max_kv_len,Hkv,D] bf16; o [B,Hq,D] bf16;
+ *   q [B,Hq,D] bf16; o [B,Hq,D] bf16;
+ *   k_cache, v_cache [B,max_kv_len,Hkv,D] of the cache dtype:
+ *     ATTN_BF16: bf16 values; k_scale and v_scale must be NULL.
+ *     ATTN_FP8_E4M3: e4m3fn codes with per-token fp32 scales k_scale, v_scale
+ *       [B,max_kv_len,Hkv] (one per key row and kv head, as the per-token-scale pages keep
+ *       one k_scale per K row): K = code * k_scale, V = code * v_scale.  Both required.
  *   kv_lens: DEVICE int32 [B], clamped in-kernel to [0, max_kv_len] (0 gives O = 0).
  *   lse: NULL or fp32 [B,Hq].
  * The KV range of every sequence is split across workgroups; each writes a partial
  * (row max, row sum, unnormalised O) to `workspace`, and a second kernel on the same
  * stream merges the partials.  workspace: device memory of at least
  * attn_decode_workspace_size(B, Hq, D, max_kv_len) bytes, owned by the caller.
- *   Supported: dtype ATTN_BF16, D == 128, Hq % Hkv == 0, Hq / Hkv <= 16.
+ *   Supported: dtype ATTN_BF16 or ATTN_FP8_E4M3, D == 128, Hq % Hkv == 0, Hq / Hkv <= 16.
  */
 size_t attn_decode_workspace_size(int B, int Hq, int D, int max_kv_len);
 int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
-                    float* lse, const int32_t* kv_lens, int dtype, int B, int Hq, int Hkv,
-                    int D, int max_kv_len, float softmax_scale, void* workspace,
+                    float* lse, const int32_t* kv_lens, const float* k_scale,
+                    const float* v_scale, int dtype, int B, int Hq, int Hkv, int D,
+                    int max_kv_len, float softmax_scale, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
 /*

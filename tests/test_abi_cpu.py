@@ -73,9 +73,9 @@ def test_prefill_validation(lib):
     assert prefill(lib, q=NUL, k=NUL, v=NUL, o=NUL, Sq=0) == OK
 
 
-def decode(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, dtype=1, B=4, Hq=32, Hkv=8, D=128, L=1024, scale=0.1,
-           ws=FAKE, wsb=1 << 40):
-    return lib.attn_decode_fwd(q, k, v, o, NUL, lens, dtype, B, Hq, Hkv, D, L, scale, ws, wsb, S)
+def decode(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, ks=NUL, vs=NUL, dtype=1, B=4, Hq=32, Hkv=8, D=128, L=1024,
+           scale=0.1, ws=FAKE, wsb=1 << 40):
+    return lib.attn_decode_fwd(q, k, v, o, NUL, lens, ks, vs, dtype, B, Hq, Hkv, D, L, scale, ws, wsb, S)
 
 
 def test_decode_validation(lib):
@@ -93,6 +93,11 @@ def test_decode_validation(lib):
     assert decode(lib, ws=NUL) == EWS
     assert decode(lib, wsb=need - 1) == EWS
     assert decode(lib, B=0, q=NUL, o=NUL, lens=NUL, ws=NUL) == OK
+    # e4m3 caches carry per-token scales; bf16 caches take none
+    assert decode(lib, dtype=2, ks=NUL, vs=FAKE) == ENULL
+    assert decode(lib, dtype=2, ks=FAKE, vs=NUL) == ENULL
+    assert decode(lib, dtype=1, ks=FAKE, vs=FAKE) == EDTYPE
+    assert decode(lib, dtype=2, ks=FAKE, vs=FAKE, D=64) == EUNSUP
 
 
 def mla_prefill(lib, qn=FAKE, qr=FAKE, kn=FAKE, kr=FAKE, v=FAKE, o=FAKE, dt=2, B=1, Sq=64, Skv=64, H=4, Hr=1,

@@ -110,3 +110,60 @@ def test_mla_decode_full_workload_sampled():
     ro, rl = oracle.mla_decode(host_f64(q[picks]), host_f64(kv[picks]), np.full(3, 4096), 512, w.scale)
     assert_close(host_f64(o[picks]), ro, BF16_TOL, "O sampled")
     assert_lse_close(lse[picks].cpu().numpy(), rl, "LSE sampled")
+
+
+# ------------------------------------------------------------------------------------------
+# e4m3 caches with per-token scales: the oracle runs on the dequantised caches (code * scale)
+
+GQA8 = "gqa_decode_fp8_b64_hq32_hkv8_d128_l8192"
+
+
+def _gqa8(w, lens=None):
+    d = make_decode(w, lens=lens)
+    t = (dev_bf16(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["kv_lens"]), dev(d["k_scale"]), dev(d["v_scale"]))
+    kd = oracle.e4m3_to_f64(d["k"]) * d["k_scale"][..., None].astype(np.float64)
+    vd = oracle.e4m3_to_f64(d["v"]) * d["v_scale"][..., None].astype(np.float64)
+    return t, kd, vd
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 1), (12, 4)])
+def test_gqa_decode_fp8_small(Hq, Hkv):
+    lens = [1, 31, 32, 33, 257, 1000, 0, 513]
+    w = workload(GQA8, B=len(lens), Hq=Hq, Hkv=Hkv, Skv=1000)
+    say(f"case gqa decode e4m3 Hq={Hq} Hkv={Hkv} lens={lens}")
+    (q, k, v, kl, ks, vs), kd, vd = _gqa8(w, lens=lens)
+    o, lse = fa.decode(q, k, v, kl, scale=w.scale, return_lse=True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(host_f64(q), kd, vd, np.asarray(lens), w.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+
+
+def test_gqa_decode_fp8_full_workload_sampled():
+    w = workload(GQA8)
+    say(f"case {w.name} (sampled sequences)")
+    (q, k, v, kl, ks, vs), kd, vd = _gqa8(w)
+    o, lse = fa.decode(q, k, v, kl, scale=w.scale, return_lse=True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    lens = kl.cpu().numpy()
+    picks = [int(np.argmin(lens)), int(np.argmax(lens)), 0, 63, 31]
+    ro, rl = [], []
+    for b in picks:
+        L = int(lens[b])
+        r, l = oracle.decode(host_f64(q[b:b + 1]), kd[b:b + 1, :L], vd[b:b + 1, :L], np.array([L]), w.scale)
+        ro.append(r[0]); rl.append(l[0])
+    assert_close(host_f64(o[picks]), np.stack(ro), BF16_TOL, "O sampled")
+    assert_lse_close(lse[picks].cpu().numpy(), np.stack(rl), "LSE sampled")
+
+
+def test_gqa_decode_fp8_matches_bf16_on_the_dequantised_cache():
+    """The e4m3 path equals the bf16 path run on the dequantised cache (rounded to bf16)."""
+    lens = [700, 129]
+    w = workload(GQA8, B=2, Skv=700)
+    (q, k, v, kl, ks, vs), kd, vd = _gqa8(w, lens=lens)
+    o8 = fa.decode(q, k, v, kl, scale=w.scale, k_scale=ks, v_scale=vs)
+    kb = torch.from_numpy(kd.astype(np.float32)).to(torch.bfloat16).cuda()
+    vb = torch.from_numpy(vd.astype(np.float32)).to(torch.bfloat16).cuda()
+    ob = fa.decode(q, kb, vb, kl, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_close(host_f64(o8), host_f64(ob), BF16_TOL, "e4m3 vs bf16 path")

@@ -102,7 +102,13 @@ def decode_lengths(w: Workload) -> np.ndarray:
 
 
 def make_decode(w: Workload, batches=None, lens=None) -> dict:
-    """GQA decode: q [nb, Hq, D]; k/v caches [nb, Lmax, Hkv, D]; kv_lens int32 [nb]."""
+    """GQA decode: q [nb, Hq, D]; k/v caches [nb, Lmax, Hkv, D]; kv_lens int32 [nb].
+
+    dtype "fp8": q in bf16; the caches as e4m3 codes with per-(token, kv head) fp32 scales
+    k_scale, v_scale [nb, Lmax, Hkv] (amax/448 of each fp32 row, the same per-row recipe as
+    the MLA prefill nope operands)."""
+    if w.dtype == "fp8":
+        return _make_decode_fp8(w, batches, lens)
     bs = _batches(w, batches)
     all_lens = decode_lengths(w) if lens is None else np.asarray(lens, np.int32)
     lens_b = np.array([all_lens[b] for b in bs], np.int32)
@@ -114,6 +120,22 @@ def make_decode(w: Workload, batches=None, lens=None) -> dict:
     _fill(w.seed, T_K, bs, w.Skv, (w.Hkv, w.D), st, [k], lens=lens_b)
     _fill(w.seed, T_V, bs, w.Skv, (w.Hkv, w.Dv), st, [v], lens=lens_b)
     return {"q": q[:, 0], "k": k, "v": v, "kv_lens": lens_b, "batches": bs}
+
+
+def _make_decode_fp8(w: Workload, batches, lens) -> dict:
+    bs = _batches(w, batches)
+    all_lens = decode_lengths(w) if lens is None else np.asarray(lens, np.int32)
+    lens_b = np.array([all_lens[b] for b in bs], np.int32)
+    nb = len(bs)
+    q = np.zeros((nb, 1, w.Hq, w.D), np.uint16)
+    k = np.zeros((nb, w.Skv, w.Hkv, w.D), np.uint8)
+    v = np.zeros((nb, w.Skv, w.Hkv, w.Dv), np.uint8)
+    ks = np.zeros((nb, w.Skv, w.Hkv), np.float32)
+    vs = np.zeros((nb, w.Skv, w.Hkv), np.float32)
+    _fill(w.seed, T_Q, bs, 1, (w.Hq, w.D), lambda x: (bf16_bits(x),), [q])
+    _fill(w.seed, T_K, bs, w.Skv, (w.Hkv, w.D), quantize_rows_e4m3, [k, ks], lens=lens_b)
+    _fill(w.seed, T_V, bs, w.Skv, (w.Hkv, w.Dv), quantize_rows_e4m3, [v, vs], lens=lens_b)
+    return {"q": q[:, 0], "k": k, "v": v, "k_scale": ks, "v_scale": vs, "kv_lens": lens_b, "batches": bs}
 
 
 def make_mla_decode(w: Workload, batches=None, lens=None) -> dict:

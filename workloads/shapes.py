@@ -14,7 +14,7 @@ class Workload:
     name: str
     kind: str                 # "prefill" | "decode" | "mla_prefill" | "mla_decode" | "quantize"
     seed: int
-    dtype: str                # storage dtype of q/k/v: "f32" | "bf16" | "fp8+bf16"
+    dtype: str                # storage dtype of q/k/v: "f32" | "bf16" | "fp8+bf16" | "fp8" (decode cache)
     B: int
     Hq: int
     Hkv: int
@@ -48,6 +48,11 @@ WORKLOADS = {
     # per-sequence lengths uniform on [1024, 8192].
     "gqa_decode_bf16_b64_hq32_hkv8_d128_l8192": Workload(
         name="gqa_decode_bf16_b64_hq32_hkv8_d128_l8192", kind="decode", seed=3, dtype="bf16",
+        B=64, Hq=32, Hkv=8, Skv=8192, D=128, Dv=128, len_lo=1024, len_hi=8192,
+        scale=1.0 / 128 ** 0.5),
+    # The same GQA decode over an e4m3 cache with per-(token, kv head) fp32 scales.
+    "gqa_decode_fp8_b64_hq32_hkv8_d128_l8192": Workload(
+        name="gqa_decode_fp8_b64_hq32_hkv8_d128_l8192", kind="decode", seed=3, dtype="fp8",
         B=64, Hq=32, Hkv=8, Skv=8192, D=128, Dv=128, len_lo=1024, len_hi=8192,
         scale=1.0 / 128 ** 0.5),
     # MLA decode: batch 64, 128 q heads over one latent head, K = [latent 512 | rope 64],
