@@ -28,7 +28,7 @@ EXPORTS = {
     "mla_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10 +
                         [ctypes.c_float, ctypes.c_void_p]),
     "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
-    "mla_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 +
+    "mla_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 +
                        [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "quantize_rows_e4m3": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_void_p]),
 }
@@ -181,10 +181,21 @@ def mla_decode_workspace_size(B: int, H: int, Dv: int, max_kv_len: int) -> int:
 
 
 def mla_decode(q, kv_cache, kv_lens, dv: int = 512, scale: float | None = None, workspace=None, out=None,
-               return_lse: bool = False):
-    """MLA decode: q [B,H,Dk] bf16, latent cache [B,Lmax,Dk] bf16 (V = first dv columns) -> o [B,H,dv]."""
-    _need(q, "q", (torch.bfloat16,), 3); _need(kv_cache, "kv_cache", (torch.bfloat16,), 3)
-    _need(kv_lens, "kv_lens", (torch.int32,), 1)
+               return_lse: bool = False, kv_scale=None):
+    """MLA decode: q [B,H,Dk] bf16, latent cache [B,Lmax,Dk] (V = first dv columns) -> o [B,H,dv].
+
+    The cache is bf16, or e4m3 codes (uint8 / float8_e4m3fn) with one fp32 scale per row,
+    kv_scale [B,Lmax]."""
+    _need(q, "q", (torch.bfloat16,), 3); _need(kv_lens, "kv_lens", (torch.int32,), 1)
+    fp8 = kv_cache.dtype in _FP8
+    if fp8:
+        _need(kv_cache, "kv_cache", _FP8, 3); _need(kv_scale, "kv_scale", (torch.float32,), 2)
+        if kv_scale.shape != kv_cache.shape[:2]:
+            raise ValueError("kv_scale must be [B, Lmax]")
+    else:
+        _need(kv_cache, "kv_cache", (torch.bfloat16,), 3)
+        if kv_scale is not None:
+            raise ValueError("kv_scale goes with an e4m3 cache only")
     B, H, Dk = q.shape
     Lmax = kv_cache.shape[1]
     if kv_cache.shape[0] != B or kv_cache.shape[2] != Dk or kv_lens.shape[0] != B:
@@ -195,7 +206,8 @@ def mla_decode(q, kv_cache, kv_lens, dv: int = 512, scale: float | None = None, 
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
-    st = lib().mla_decode_fwd(_ptr(q), _ptr(kv_cache), _ptr(o), _ptr(lse), _ptr(kv_lens), B, H, Dk, dv, Lmax,
+    st = lib().mla_decode_fwd(_ptr(q), _ptr(kv_cache), _ptr(o), _ptr(lse), _ptr(kv_lens), _ptr(kv_scale),
+                              ATTN_FP8_E4M3 if fp8 else ATTN_BF16, B, H, Dk, dv, Lmax,
                               scale, _ptr(workspace), workspace.numel(), _stream())
     _check("mla_decode_fwd", st)
     return (o, lse) if return_lse else o

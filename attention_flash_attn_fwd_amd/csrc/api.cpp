@@ -126,15 +126,19 @@ size_t mla_decode_workspace_size(int B, int H, int Dv, int max_kv_len) {
   return fa::decode_workspace_bytes(B, H, Dv, p.n_split);
 }
 
-int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, const int32_t* kv_lens, int B, int H,
-                   int Dk, int Dv, int max_kv_len, float softmax_scale, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, const int32_t* kv_lens,
+                   const float* kv_scale, int dtype, int B, int H, int Dk, int Dv, int max_kv_len,
+                   float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
+  const bool fp8 = dtype == ATTN_FP8_E4M3;
+  if (!fp8 && kv_scale) return ATTN_ERR_DTYPE;  // the scale belongs to e4m3 caches only
   if (B < 0 || H <= 0 || Dk <= 0 || Dv <= 0 || max_kv_len < 0 || Dv > Dk) return ATTN_ERR_SHAPE;
   if (elems({B, max_kv_len, Dk}) < 0 || elems({B, H, Dk}) < 0) return ATTN_ERR_SHAPE;
   if (Dk != 576 || Dv != 512 || H % 16 != 0 || H > 128) return ATTN_ERR_UNSUPPORTED;
   if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
   if (B == 0) return ATTN_OK;
   if (!q || !o || !kv_lens || (max_kv_len > 0 && !kv_cache)) return ATTN_ERR_NULL;
+  if (fp8 && max_kv_len > 0 && !kv_scale) return ATTN_ERR_NULL;
   const fa::SplitPlan p = fa::mla_decode_plan(B, H, max_kv_len);
   if (B > 65535 || elems({p.n_split, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
   if (elems({B, H, Dv}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
@@ -142,12 +146,13 @@ int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, con
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   fa::DecodeArgs a{};
   a.q = q; a.k = kv_cache; a.v = nullptr; a.o = o; a.lse = lse; a.kv_lens = kv_lens;
+  a.k_scale = kv_scale;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + ((size_t)B * H * p.n_split * Dv * 4 + 255) / 256 * 256);
   a.B = B; a.Hq = H; a.Hkv = 1; a.max_len = max_kv_len;
   a.n_split = p.n_split; a.chunk = p.chunk;
   a.scale = softmax_scale;
-  return hip_status(fa::launch_mla_decode(a, false, stream));
+  return hip_status(fa::launch_mla_decode(a, fp8, stream));
 }
 
 int quantize_rows_e4m3(const float* x, uint8_t* codes, float* scale, int n_rows, int cols, hipStream_t stream) {

@@ -590,6 +590,209 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// MLA decode split over an e4m3 latent cache with one fp32 scale per cache row
+// (kv_scale [B, max_len]; the row serves as K and, through its first 512 columns, as V, so
+// K = code * scale and V = code[:512] * scale).  Same wave-pair layout as the bf16 kernel
+// at half the bytes per key:
+//  * LDS rows are the 576 code bytes, unpadded; 16-byte chunk q of row r sits at chunk
+//    q ^ ((r >> 2) & 3) (within its aligned group of four), which keeps both read
+//    patterns below free of bank conflicts;
+//  * S^T A operand: one 16-byte read gives a lane 16 consecutive latent columns, i.e. its
+//    halves of two 32x32x16 steps (the contraction order is permuted: block p, lane half
+//    hl, step u, element i is column 32p + 16hl + 8u + i, and Q^T uses the same order);
+//    the pair splits the blocks p by parity;
+//  * V^T A operand: one ds_read_b64_tr_b8 per product (8 keys of one column per lane);
+//  * codes convert exactly to bf16; the row scale multiplies S and is folded into P.
+
+constexpr int M8_ROWB = 576;                         // e4m3 latent row
+constexpr int M8_TILE = TK * M8_ROWB;                // 18 KiB per stage
+constexpr int M8_BLKS = M8_TILE / 1024;              // 18 one-KiB direct copies per tile
+constexpr int M8_OPS = (M8_BLKS + MLA_NW - 1) / MLA_NW;  // 3 per wave (spare slots: scales, dummy)
+constexpr int M8_SC = 256;                           // scale copy: 64 lanes x 4 bytes
+constexpr int M8_STAGE = M8_TILE + M8_SC;
+constexpr int M8_KR = MLA_DK / 32 / 2;               // 16-byte K reads per wave per tile (9)
+
+__device__ __forceinline__ uint32_t m8_chunk(uint32_t row, uint32_t q) { return q ^ ((row >> 2) & 3u); }
+
+__global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char st0_raw[M8_STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1_raw[M8_STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2_raw[M8_STAGE];
+  __shared__ __attribute__((aligned(1024))) char xs_raw[MLA_NW * 4096];  // partial S^T per wave
+  __shared__ __attribute__((aligned(1024))) char dummy_raw[1024];         // target of spare copies
+  FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw};
+
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int L = min(max(a.kv_lens[b], 0), a.max_len);
+  const int start = split * a.chunk;
+  if (start >= L) return;  // uniform over the workgroup
+  const int end = min(start + a.chunk, L);
+  const int n_tiles = (end - start + TK - 1) / TK;
+
+  const int wave = wave_id(), lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
+  const int hh = wave >> 2;
+  const int h = 32 * (wave & 3) + l32;
+  const bool hvalid = h < a.Hq;
+  const float c = a.scale * kLog2e;
+
+  // Q^T half as the B operand: block p = 2i + hh, step u: latent columns 32p + 16hl + 8u .. +7
+  i32x4_t qf[M8_KR][2];
+  {
+    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * (MLA_DK * 2);
+#pragma unroll
+    for (int i = 0; i < M8_KR; i++)
+#pragma unroll
+      for (int u = 0; u < 2; u++) qf[i][u] = *(const i32x4_t*)(qp + (32 * (2 * i + hh) + 16 * hl + 8 * u) * 2);
+  }
+  const char* kv = (const char*)a.k + (size_t)b * a.max_len * M8_ROWB;
+  const float* ksb = a.k_scale + (size_t)b * a.max_len;
+  // direct copies of a tile: block blk < 18 of LDS bytes [1024 blk, +1024) is row o / 576,
+  // physical chunk (o % 576) / 16 for o = 1024 blk + 16 lane; the spare third copy of
+  // wave 2 brings the tile's row scales, the other spares land in a dummy buffer, so every
+  // wave issues the same number of copies per tile
+  auto issue = [&](int t, FA_LDS char* dst) {
+    const int key0 = start + t * TK, valid = min(TK, end - key0);
+    const auto r = make_rsrc(kv + (size_t)key0 * M8_ROWB, (uint32_t)valid * M8_ROWB);
+#pragma unroll
+    for (int i = 0; i < M8_OPS; i++) {
+      const int blk = i * MLA_NW + wave;
+      if (blk < M8_BLKS) {
+        const uint32_t o = blk * 1024 + lane * 16;
+        const uint32_t row = o / M8_ROWB, pc = (o % M8_ROWB) >> 4;
+        const uint32_t rc = min(row, (uint32_t)(valid - 1));  // rows past the sequence repeat its last row
+        dma16_buf(r, dst + blk * 1024, rc * M8_ROWB + m8_chunk(row, pc) * 16);
+      } else if (blk == M8_BLKS) {
+        const auto rs = make_rsrc(ksb + key0, (uint32_t)valid * 4);
+        dma4_buf(rs, dst + M8_TILE, (uint32_t)min(lane, valid - 1) * 4);
+      } else {
+        dma16_buf(r, (FA_LDS char*)dummy_raw, 0);
+      }
+    }
+  };
+  // S^T A operand: key row l32, logical chunk 4i + 2hh + hl; the XOR touches only the two
+  // low chunk bits, so read i sits at one base plus 64i bytes
+  const uint32_t kaddr = l32 * M8_ROWB + (((2 * hh + hl) ^ ((l32 >> 2) & 3)) << 4);
+  // V^T reads: 16-lane group G = lane / 16 (hl = G / 2, column half dh = G % 2); lane 2e + h
+  // of the group reads key row 16tp + 8(e/4) + 4hl + e%4 at byte 8h of chunk
+  // 16hh + 2db + dh, so output byte e of lane l is column 256hh + 32db + l%32 of that key
+  // (16hh + 4(db/2) + dh + 2(db%2) after the XOR: one base per key step and block parity
+  // plus 64(db/2) bytes)
+  uint32_t vaddr[2][2];
+  {
+    const uint32_t G = lane >> 4, e = (lane & 15) >> 1, hb = lane & 1;
+#pragma unroll
+    for (int tp = 0; tp < 2; tp++) {
+      const uint32_t row = 16 * tp + 8 * (e >> 2) + 4 * (G >> 1) + (e & 3);
+      const uint32_t x = (G & 1) ^ ((row >> 2) & 3);
+      vaddr[tp][0] = row * M8_ROWB + 8 * hb + ((16 * hh + x) << 4);
+      vaddr[tp][1] = row * M8_ROWB + 8 * hb + ((16 * hh + (x ^ 2)) << 4);
+    }
+  }
+
+  float m_ref = -INFINITY, neg = 0.f, l = 0.f;
+  f32x16_t o[MLA_DB];
+#pragma unroll
+  for (int d = 0; d < MLA_DB; d++) o[d] = f32x16_t{};
+  FA_LDS char* const xs_own = (FA_LDS char*)xs_raw + wave * 4096 + lane * 16;
+  const FA_LDS char* const xs_peer = (FA_LDS char*)xs_raw + (wave ^ 4) * 4096 + lane * 16;
+
+  auto tile = [&](auto SLOT, int t) {
+    constexpr int sl = decltype(SLOT)::value;
+    if (t + 1 < n_tiles) wait_vmcnt<M8_OPS>();
+    else wait_vmcnt<0>();
+    barrier();
+    if (t + 2 < n_tiles) issue(t + 2, st[(sl + 2) % MLA_NS]);
+    const FA_LDS char* kt = st[sl];
+    f32x16_t s{};
+#pragma unroll
+    for (int i = 0; i < M8_KR; i++) {
+      const i32x4_t w = lds_b128(kt + kaddr + 64 * i);
+      s = mfma32x32x16_bf16(e4m3x8_to_bf16(i32x2_t{w.x, w.y}), qf[i][0], s);
+      s = mfma32x32x16_bf16(e4m3x8_to_bf16(i32x2_t{w.z, w.w}), qf[i][1], s);
+      if (i % 3 == 2) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) *(FA_LDS f32x4_t*)(xs_own + 1024 * j) = f32x4_t{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
+    barrier();
+    // register v holds key 8(v/4) + 4hl + v%4 of the tile; its row scale scales S and P
+    f32x4_t sc[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const f32x4_t pv = lds_f32x4(xs_peer + 1024 * j);
+      sc[j] = lds_f32x4(kt + M8_TILE + (8 * j + 4 * hl) * 4);
+#pragma unroll
+      for (int v = 0; v < 4; v++) s[4 * j + v] = (s[4 * j + v] + pv[v]) * sc[j][v];
+    }
+    const int key0 = start + t * TK;
+    if (key0 + TK > end) {
+      const int lim = end - key0 - 4 * hl;
+#pragma unroll
+      for (int v = 0; v < 16; v++) s[v] = (8 * (v >> 2) + (v & 3)) < lim ? s[v] : -INFINITY;
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; v++) mx = fmaxf(mx, s[v]);
+    mx = xor32_max(mx);
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_ref * c + 8.f)) {  // lazy rescale (P <= 2^8)
+      const float m_new = fmaxf(m_ref, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast((m_ref - m_use) * c);
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < MLA_DB; d++) o[d] *= alpha;
+      m_ref = m_new;
+      neg = -m_use * c;
+    }
+    i32x4_t pb[2];
+#pragma unroll
+    for (int tp = 0; tp < 2; tp++) {
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        e[i] = exp2_fast(fmaf(s[8 * tp + i], c, neg));
+        l += e[i];
+      }
+      const f32x4_t s0 = sc[2 * tp], s1 = sc[2 * tp + 1];
+      pb[tp] = i32x4_t{pack_bf16(e[0] * s0[0], e[1] * s0[1]), pack_bf16(e[2] * s0[2], e[3] * s0[3]),
+                       pack_bf16(e[4] * s1[0], e[5] * s1[1]), pack_bf16(e[6] * s1[2], e[7] * s1[3])};
+    }
+#pragma unroll
+    for (int tp = 0; tp < 2; tp++)
+#pragma unroll
+      for (int db = 0; db < MLA_DB; db++) {
+        const i32x2_t w = lds_tr8(kt + vaddr[tp][db & 1] + 64 * (db >> 1));
+        o[db] = mfma32x32x16_bf16(e4m3x8_to_bf16(w), pb[tp], o[db]);
+        if (db % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  issue(0, st[0]);
+  if (1 < n_tiles) issue(1, st[1]);
+  for (int t = 0; t < n_tiles; t += 3) {
+    tile(std::integral_constant<int, 0>{}, t);
+    if (t + 1 >= n_tiles) break;
+    tile(std::integral_constant<int, 1>{}, t + 1);
+    if (t + 2 >= n_tiles) break;
+    tile(std::integral_constant<int, 2>{}, t + 2);
+  }
+
+  const float l_tot = xor32_sum(l);
+  if (hvalid) {
+    const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + split;
+    float* po = a.part_o + pidx * MLA_DV + 256 * hh + 4 * hl;
+#pragma unroll
+    for (int db = 0; db < MLA_DB; db++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        *(f32x4_t*)(po + 32 * db + 8 * j) = f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
+    if (hh == 0 && hl == 0) {
+      a.part_ml[2 * pidx] = m_ref;
+      a.part_ml[2 * pidx + 1] = l_tot;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Combine: merges, for every (batch, head) row, the splits that cover [0, L_b) in split
 // order (deterministic, no atomics): O = sum_s w_s O_s / sum_s w_s l_s with
 // w_s = exp2((m_s - M) c), M = max_s m_s.  A thread owns 8 consecutive output columns of
@@ -684,9 +887,9 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
 }
 
 hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
-  if (fp8) return hipErrorInvalidValue;
   dim3 grid(a.n_split, a.B);
-  mla_decode_split<<<grid, 64 * MLA_NW, 0, s>>>(a);
+  if (fp8) mla_decode_split_fp8<<<grid, 64 * MLA_NW, 0, s>>>(a);
+  else mla_decode_split<<<grid, 64 * MLA_NW, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   combine_kernel<<<(a.B * a.Hq * (MLA_DV / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, MLA_DV);

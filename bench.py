@@ -55,7 +55,10 @@ def algorithmic_work(w, lens=None):
     if w.kind == "mla_decode":
         sl = int(sum(lens))
         flops = 2 * w.Hq * (w.D + w.Dv) * sl
-        byts = sl * w.D * 2 + w.B * w.Hq * (w.D + w.Dv) * 2
+        if w.dtype == "fp8":   # e4m3 latent rows plus one fp32 scale per row
+            byts = sl * (w.D + 4) + w.B * w.Hq * (w.D + w.Dv) * 2
+        else:
+            byts = sl * w.D * 2 + w.B * w.Hq * (w.D + w.Dv) * 2
         return flops, byts
     if w.kind == "mla_prefill":
         pairs = w.Sq * (w.Sq + 1) // 2 if w.causal else w.Sq * w.Skv
@@ -118,13 +121,18 @@ def setup(w):
     if w.kind == "mla_decode":
         d = make_mla_decode(w)
         q, kv_lens = bf16(d["q"]), torch.from_numpy(d["kv_lens"]).cuda()
-        # two copies of the 302 MB latent cache, alternated, so the 256 MB MALL cannot serve a step
-        kv0 = bf16(d["kv"])
+        # two copies of the latent cache (302 MB bf16, 151 MB e4m3), alternated, so that the
+        # 256 MB MALL cannot serve a step from the previous one
+        fp8 = w.dtype == "fp8"
+        kv0 = torch.from_numpy(d["kv"]).cuda() if fp8 else bf16(d["kv"])
         caches = [kv0, kv0.clone()]
+        scales = [torch.from_numpy(d["kv_scale"]).cuda()] * 2 if fp8 else [None, None]
+        if fp8:
+            scales[1] = scales[0].clone()
         ws = torch.empty(fa.mla_decode_workspace_size(w.B, w.Hq, w.Dv, w.Skv), dtype=torch.uint8, device="cuda")
         o = torch.empty((w.B, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda")
-        return (lambda i: fa.mla_decode(q, caches[i & 1], kv_lens, dv=w.Dv, scale=w.scale, workspace=ws, out=o)), \
-            d["kv_lens"], (q, caches, ws, o)
+        return (lambda i: fa.mla_decode(q, caches[i & 1], kv_lens, dv=w.Dv, scale=w.scale, workspace=ws, out=o,
+                                        kv_scale=scales[i & 1])), d["kv_lens"], (q, caches, scales, ws, o)
     if w.kind == "mla_prefill":
         d = make_mla_prefill(w)
         t = {n: (bf16(d[n]) if d[n].dtype == np.uint16 else torch.from_numpy(d[n]).cuda())
@@ -219,7 +227,11 @@ def cpu_baseline(w, lens, budget_s: float):
         else:
             d = make_mla_decode(w, batches=[b], lens=lens)
             L = int(d["kv_lens"][0])
-            args = (oracle.bf16_to_f64(d["q"]), oracle.bf16_to_f64(d["kv"][:, :L]), d["kv_lens"], w.Dv, w.scale)
+            if w.dtype == "fp8":
+                kv = oracle.e4m3_to_f64(d["kv"][:, :L]) * d["kv_scale"][:, :L, None].astype(np.float64)
+            else:
+                kv = oracle.bf16_to_f64(d["kv"][:, :L])
+            args = (oracle.bf16_to_f64(d["q"]), kv, d["kv_lens"], w.Dv, w.scale)
             fn = oracle.mla_decode
         t0 = time.perf_counter()
         fn(*args)

@@ -122,16 +122,22 @@ int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope,
  * MLA decode (KVPipelineGeneric page, MLA decode utilities): H query heads share one
  * latent KV head; a cache row is [latent Dv | rope Dk-Dv] and serves as K (all Dk
  * columns) and as V (its first Dv columns), read from HBM once.
- *   q [B,H,Dk] bf16; kv_cache [B,max_kv_len,Dk] bf16; o [B,H,Dv] bf16;
+ *   q [B,H,Dk] bf16; o [B,H,Dv] bf16;
+ *   kv_cache [B,max_kv_len,Dk] of the cache dtype:
+ *     ATTN_BF16: bf16 values; kv_scale must be NULL.
+ *     ATTN_FP8_E4M3: e4m3fn codes with one fp32 scale per cache row, kv_scale
+ *       [B,max_kv_len] (the row is one token's latent K and V, so its scale serves both):
+ *       K = code * kv_scale, V = code[:Dv] * kv_scale.  Required.
  *   kv_lens DEVICE int32 [B] (clamped to [0, max_kv_len]); lse NULL or fp32 [B,H].
  *   workspace: at least mla_decode_workspace_size(B, H, Dv, max_kv_len) bytes.
- *   Supported: (Dk, Dv) == (576, 512), H % 16 == 0, H <= 128.
+ *   Supported: dtype ATTN_BF16 or ATTN_FP8_E4M3, (Dk, Dv) == (576, 512), H % 16 == 0,
+ *   H <= 128.
  */
 size_t mla_decode_workspace_size(int B, int H, int Dv, int max_kv_len);
 int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse,
-                   const int32_t* kv_lens, int B, int H, int Dk, int Dv, int max_kv_len,
-                   float softmax_scale, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream);
+                   const int32_t* kv_lens, const float* kv_scale, int dtype, int B, int H,
+                   int Dk, int Dv, int max_kv_len, float softmax_scale, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Per-token e4m3 quantisation: produces the nope operands and scales that

@@ -119,9 +119,9 @@ def test_mla_prefill_validation(lib):
     assert mla_prefill(lib, B=0, qn=NUL, qr=NUL, kn=NUL, kr=NUL, v=NUL, o=NUL) == OK
 
 
-def mla_decode(lib, q=FAKE, kv=FAKE, o=FAKE, lens=FAKE, B=8, H=128, Dk=576, Dv=512, L=4096, scale=0.04, ws=FAKE,
-               wsb=1 << 40):
-    return lib.mla_decode_fwd(q, kv, o, NUL, lens, B, H, Dk, Dv, L, scale, ws, wsb, S)
+def mla_decode(lib, q=FAKE, kv=FAKE, o=FAKE, lens=FAKE, ks=NUL, dtype=1, B=8, H=128, Dk=576, Dv=512, L=4096,
+               scale=0.04, ws=FAKE, wsb=1 << 40):
+    return lib.mla_decode_fwd(q, kv, o, NUL, lens, ks, dtype, B, H, Dk, Dv, L, scale, ws, wsb, S)
 
 
 def test_mla_decode_validation(lib):
@@ -135,6 +135,13 @@ def test_mla_decode_validation(lib):
     assert mla_decode(lib, kv=NUL) == ENULL
     assert mla_decode(lib, wsb=need - 1) == EWS
     assert mla_decode(lib, B=0, q=NUL, kv=NUL, o=NUL, lens=NUL, ws=NUL) == OK
+    # e4m3 latent caches carry one scale per row; bf16 caches take none
+    assert mla_decode(lib, dtype=0) == EDTYPE
+    assert mla_decode(lib, dtype=3, ks=FAKE) == EDTYPE
+    assert mla_decode(lib, dtype=2, ks=NUL) == ENULL
+    assert mla_decode(lib, dtype=1, ks=FAKE) == EDTYPE
+    assert mla_decode(lib, dtype=2, ks=FAKE, Dk=512) == EUNSUP
+    assert mla_decode(lib, dtype=2, ks=FAKE, wsb=need - 1) == EWS
 
 
 def test_quantize_validation(lib):

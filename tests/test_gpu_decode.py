@@ -167,3 +167,60 @@ def test_gqa_decode_fp8_matches_bf16_on_the_dequantised_cache():
     ob = fa.decode(q, kb, vb, kl, scale=w.scale)
     torch.cuda.synchronize()
     assert_close(host_f64(o8), host_f64(ob), BF16_TOL, "e4m3 vs bf16 path")
+
+
+MLA8 = "mla_decode_fp8_b64_h128_dk576_dv512_l4096"
+
+
+def _mla8(w, lens=None):
+    d = make_mla_decode(w, lens=lens)
+    t = (dev_bf16(d["q"]), dev(d["kv"]), dev(d["kv_lens"]), dev(d["kv_scale"]))
+    return t, oracle.e4m3_to_f64(d["kv"]) * d["kv_scale"][..., None].astype(np.float64)
+
+
+@pytest.mark.parametrize("H", [128, 16, 48, 112])
+def test_mla_decode_fp8_small(H):
+    lens = [1, 33, 300, 0, 128, 31, 32, 255]
+    w = workload(MLA8, B=len(lens), Hq=H, Skv=300)
+    say(f"case mla decode e4m3 H={H} lens={lens}")
+    (q, kv, kl, ks), kvd = _mla8(w, lens=lens)
+    o, lse = fa.mla_decode(q, kv, kl, dv=512, scale=w.scale, return_lse=True, kv_scale=ks)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode(host_f64(q), kvd, np.asarray(lens), 512, w.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+
+
+def test_mla_decode_fp8_long_single_sequence():
+    w = workload(MLA8, B=1, Skv=9000)
+    say(f"case mla decode e4m3 B=1 len=8999")
+    (q, kv, kl, ks), kvd = _mla8(w, lens=[8999])
+    o, lse = fa.mla_decode(q, kv, kl, dv=512, scale=w.scale, return_lse=True, kv_scale=ks)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode(host_f64(q), kvd, np.array([8999]), 512, w.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+
+
+def test_mla_decode_fp8_full_workload_sampled():
+    w = workload(MLA8)
+    say(f"case {w.name} (sampled sequences)")
+    (q, kv, kl, ks), kvd = _mla8(w)
+    o, lse = fa.mla_decode(q, kv, kl, dv=512, scale=w.scale, return_lse=True, kv_scale=ks)
+    torch.cuda.synchronize()
+    picks = [0, 37, 63]
+    ro, rl = oracle.mla_decode(host_f64(q[picks]), kvd[picks], np.full(3, 4096), 512, w.scale)
+    assert_close(host_f64(o[picks]), ro, BF16_TOL, "O sampled")
+    assert_lse_close(lse[picks].cpu().numpy(), rl, "LSE sampled")
+
+
+def test_mla_decode_fp8_matches_bf16_on_the_dequantised_cache():
+    """The e4m3 path equals the bf16 path run on the dequantised cache (rounded to bf16)."""
+    lens = [700, 97]
+    w = workload(MLA8, B=2, Skv=700)
+    (q, kv, kl, ks), kvd = _mla8(w, lens=lens)
+    o8 = fa.mla_decode(q, kv, kl, dv=512, scale=w.scale, kv_scale=ks)
+    kvb = torch.from_numpy(kvd.astype(np.float32)).to(torch.bfloat16).cuda()
+    ob = fa.mla_decode(q, kvb, kl, dv=512, scale=w.scale)
+    torch.cuda.synchronize()
+    assert_close(host_f64(o8), host_f64(ob), BF16_TOL, "e4m3 vs bf16 path")

@@ -141,12 +141,22 @@ def _make_decode_fp8(w: Workload, batches, lens) -> dict:
 def make_mla_decode(w: Workload, batches=None, lens=None) -> dict:
     """MLA decode: q [nb, H, Dk]; latent cache kv [nb, Lmax, Dk]; kv_lens int32 [nb].
 
-    V is not a tensor of its own: it is kv[..., :Dv].
+    V is not a tensor of its own: it is kv[..., :Dv].  dtype "fp8": q in bf16; the cache as
+    e4m3 codes with one fp32 scale per row, kv_scale [nb, Lmax] (amax/448 of the whole
+    fp32 latent row, the per-row recipe of the other e4m3 operands).
     """
     bs = _batches(w, batches)
     all_lens = decode_lengths(w) if lens is None else np.asarray(lens, np.int32)
     lens_b = np.array([all_lens[b] for b in bs], np.int32)
-    nb, st, dt = len(bs), _store_fn(w.dtype), _np_dtype(w.dtype)
+    nb = len(bs)
+    if w.dtype == "fp8":
+        q = np.zeros((nb, 1, w.Hq, w.D), np.uint16)
+        kv = np.zeros((nb, w.Skv, w.D), np.uint8)
+        kvs = np.zeros((nb, w.Skv), np.float32)
+        _fill(w.seed, T_Q, bs, 1, (w.Hq, w.D), lambda x: (bf16_bits(x),), [q])
+        _fill(w.seed, T_KV, bs, w.Skv, (w.D,), quantize_rows_e4m3, [kv, kvs], lens=lens_b)
+        return {"q": q[:, 0], "kv": kv, "kv_scale": kvs, "kv_lens": lens_b, "batches": bs}
+    st, dt = _store_fn(w.dtype), _np_dtype(w.dtype)
     q = np.zeros((nb, 1, w.Hq, w.D), dt)
     kv = np.zeros((nb, w.Skv, w.D), dt)
     _fill(w.seed, T_Q, bs, 1, (w.Hq, w.D), st, [q])

@@ -61,6 +61,11 @@ WORKLOADS = {
         name="mla_decode_bf16_b64_h128_dk576_dv512_l4096", kind="mla_decode", seed=4, dtype="bf16",
         B=64, Hq=128, Hkv=1, Skv=4096, D=576, Dv=512, len_lo=4096, len_hi=4096,
         scale=1.0 / 576 ** 0.5),
+    # The same MLA decode over an e4m3 latent cache with one fp32 scale per cache row (token).
+    "mla_decode_fp8_b64_h128_dk576_dv512_l4096": Workload(
+        name="mla_decode_fp8_b64_h128_dk576_dv512_l4096", kind="mla_decode", seed=4, dtype="fp8",
+        B=64, Hq=128, Hkv=1, Skv=4096, D=576, Dv=512, len_lo=4096, len_hi=4096,
+        scale=1.0 / 576 ** 0.5),
     # MLA prefill, causal, per-token scales: batch 1, 128 heads, seq 8192; nope 128 in e4m3 with
     # per-(token, head) fp32 scales, rope 64 in bf16 (one shared k_rope head), V 128 in bf16.
     "mla_prefill_fp8_causal_b1_h128_s8192": Workload(
