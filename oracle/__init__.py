@@ -15,7 +15,9 @@ never print the softmax, so the textbook definition stands in for it.  The
 oracle never blocks over keys (that would be the online algorithm it checks).
 
 It also holds the per-token e4m3 quantiser (oracle/quantize.py) that produces the
-MLA prefill nope operands and their fp32 scales.
+MLA prefill nope operands and their fp32 scales, and (oracle/ragged.py) ragged-batch
+prefill over packed sequences and the merge of two partial attention results by
+their LSE.
 
 parity pins: see tests/test_oracle_*.py (brute force, torch CPU fp64 SDPA,
 closed forms, invariants, the OCP e4m3 code table, torch float8 casts).
@@ -31,8 +33,10 @@ from .attention import (
     mla_prefill_rows,
     mla_decode,
 )
+from .ragged import merge_states, prefill_varlen
 
 __all__ = [
     "bf16_to_f64", "e4m3_to_f64", "E4M3_TABLE", "e4m3_round", "quantize_rows", "row_scale",
     "sdpa_rows", "prefill", "prefill_rows", "decode", "mla_prefill", "mla_prefill_rows", "mla_decode",
+    "prefill_varlen", "merge_states",
 ]
