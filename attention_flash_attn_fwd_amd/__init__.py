@@ -22,6 +22,9 @@ EXPORTS = {
     "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "attn_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 4 + [ctypes.c_void_p] + [ctypes.c_int] * 8 +
                          [ctypes.c_float, ctypes.c_void_p]),
+    "attn_prefill_varlen_fwd": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 9 +
+                                [ctypes.c_float, ctypes.c_void_p]),
+    "attn_merge_fwd": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 5 + [ctypes.c_void_p]),
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "attn_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -105,6 +108,46 @@ def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None,
                                 int(bool(causal)), scale, _stream())
     _check("attn_prefill_fwd", st)
     return (o, lse) if return_lse else o
+
+
+def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                   scale: float | None = None, out=None, return_lse: bool = False):
+    """Ragged-batch prefill over packed sequences.  q [Tq,Hq,D], k/v [Tk,Hkv,D] bf16;
+    cu_seqlens_q/k int32 [B+1] (device) -> o [Tq,Hq,D] (and lse [Hq,Tq])."""
+    _need(q, "q", (torch.bfloat16,), 3); _need(k, "k", (torch.bfloat16,), 3); _need(v, "v", (torch.bfloat16,), 3)
+    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), 1); _need(cu_seqlens_k, "cu_seqlens_k", (torch.int32,), 1)
+    Tq, Hq, D = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.shape[0] - 1
+    if B < 0 or cu_seqlens_k.shape[0] != B + 1 or k.shape[2] != D or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if return_lse else None
+    st = lib().attn_prefill_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                                       _ptr(cu_seqlens_k), ATTN_BF16, B, Tq, Tk, int(max_seqlen_q), Hq, Hkv, D,
+                                       int(bool(causal)), scale, _stream())
+    _check("attn_prefill_varlen_fwd", st)
+    return (o, lse) if return_lse else o
+
+
+def merge(o_a, lse_a, o_b, lse_b, out=None, out_lse=None, return_lse: bool = False):
+    """Merge two partial attention results over disjoint key sets: o_* [B,S,H,D] (bf16 or fp32),
+    lse_* [B,H,S] fp32 -> o [B,S,H,D] (and lse [B,H,S]).  out / out_lse may be o_a / lse_a."""
+    dts = (torch.bfloat16, torch.float32)
+    _need(o_a, "o_a", dts, 4); _need(o_b, "o_b", (o_a.dtype,), 4)
+    _need(lse_a, "lse_a", (torch.float32,), 3); _need(lse_b, "lse_b", (torch.float32,), 3)
+    B, S, H, D = o_a.shape
+    if o_b.shape != o_a.shape or tuple(lse_a.shape) != (B, H, S) or lse_b.shape != lse_a.shape:
+        raise ValueError("shape mismatch")
+    o = torch.empty_like(o_a) if out is None else out
+    lse = out_lse
+    if lse is None and return_lse:
+        lse = torch.empty_like(lse_a)
+    st = lib().attn_merge_fwd(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse),
+                              ATTN_BF16 if o_a.dtype == torch.bfloat16 else ATTN_F32, B, S, H, D, _stream())
+    _check("attn_merge_fwd", st)
+    return (o, lse) if (return_lse or out_lse is not None) else o
 
 
 def decode_workspace_size(B: int, Hq: int, D: int, max_kv_len: int) -> int:

@@ -62,6 +62,47 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
   return hip_status(dtype == ATTN_BF16 ? fa::launch_prefill_bf16(a, D, stream) : fa::launch_prefill_f32(a, D, stream));
 }
 
+int attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, int B, int total_q,
+                            int total_k, int max_seqlen_q, int Hq, int Hkv, int D, int causal, float softmax_scale,
+                            hipStream_t stream) {
+  if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (B < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0)
+    return ATTN_ERR_SHAPE;
+  if (elems({total_q, Hq, D}) < 0 || elems({total_k, Hkv, D}) < 0) return ATTN_ERR_SHAPE;
+  if (elems({(max_seqlen_q + 127) / 128, (int64_t)(B * (int64_t)Hq + 7) / 8 * 8}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
+  if (B == 0 || total_q == 0 || max_seqlen_q == 0) return ATTN_OK;
+  if (!q || !o || !cu_seqlens_q || !cu_seqlens_k || (total_k > 0 && (!k || !v))) return ATTN_ERR_NULL;
+  fa::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.cu_q = cu_seqlens_q; a.cu_k = cu_seqlens_k;
+  a.total_q = total_q; a.total_k = total_k;
+  a.B = B; a.Sq = max_seqlen_q; a.Skv = 0; a.Hq = Hq; a.Hkv = Hkv; a.Hr = 1;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale;
+  return hip_status(fa::launch_prefill_varlen_bf16(a, D, stream));
+}
+
+int attn_merge_fwd(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                   int dtype, int B, int S, int H, int D, hipStream_t stream) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+  if (B < 0 || S < 0 || H <= 0 || D <= 0) return ATTN_ERR_SHAPE;
+  const int64_t n = elems({B, S, H, D});
+  if (n < 0 || n > (int64_t)INT32_MAX * 64) return ATTN_ERR_SHAPE;
+  const int esz = dtype == ATTN_BF16 ? 2 : 4;
+  const int chunks = D * esz / 16;  // 16-byte chunks per row: a power of two up to 64
+  if ((D * esz) % 16 != 0 || chunks > 64 || (chunks & (chunks - 1)) != 0) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!o_a || !lse_a || !o_b || !lse_b || !o) return ATTN_ERR_NULL;
+  fa::MergeArgs a{};
+  a.o_a = o_a; a.lse_a = lse_a; a.o_b = o_b; a.lse_b = lse_b; a.o = o; a.lse = lse;
+  a.B = B; a.S = S; a.H = H; a.D = D;
+  a.log2_chunks = __builtin_ctz((unsigned)chunks);
+  return hip_status(fa::launch_merge(a, dtype == ATTN_BF16, stream));
+}
+
 size_t attn_decode_workspace_size(int B, int Hq, int D, int max_kv_len) {
   if (B < 0 || Hq <= 0 || D <= 0 || max_kv_len < 0) return 0;
   const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);

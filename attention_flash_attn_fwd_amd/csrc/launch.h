@@ -17,7 +17,10 @@ struct PrefillArgs {
   const void* k_rope;   // MLA only
   const float* q_scale; // MLA only, nullable (= 1)
   const float* k_scale; // MLA only, nullable (= 1)
-  int B, Sq, Skv, Hq, Hkv, Hr;
+  const int32_t* cu_q;  // ragged batches only: query / key row offsets [B+1] of each sequence
+  const int32_t* cu_k;
+  int total_q, total_k; // ragged batches: rows of the packed q and k/v tensors
+  int B, Sq, Skv, Hq, Hkv, Hr;  // ragged batches: Sq = the longest query sequence
   int causal;
   float scale;
 };
@@ -38,6 +41,17 @@ struct DecodeArgs {
   float scale;
 };
 
+struct MergeArgs {
+  const void* o_a;      // [B, S, H, D] partial outputs over two disjoint key sets
+  const float* lse_a;   // [B, H, S]
+  const void* o_b;
+  const float* lse_b;
+  void* o;              // [B, S, H, D] merged output (may alias o_a or o_b)
+  float* lse;           // [B, H, S] merged LSE, nullable (may alias lse_a or lse_b)
+  int B, S, H, D;
+  int log2_chunks;      // log2 of the 16-byte chunks per output row (0..6)
+};
+
 struct QuantArgs {
   const float* x;       // [n_rows, cols] fp32
   uint8_t* codes;       // [n_rows, cols] e4m3fn
@@ -48,7 +62,9 @@ struct QuantArgs {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t s);
+hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);
 int quantize_lanes_per_row(int cols);
 hipError_t launch_quantize_rows(const QuantArgs& a, hipStream_t s);
 

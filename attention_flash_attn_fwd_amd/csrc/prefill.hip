@@ -316,8 +316,11 @@ __device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFr
 
 // ------------------------------------------------------------------------------------
 
-template <class QK, int DV, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qblocks) {
+// VARLEN: a ragged batch of packed sequences; sequence b owns query rows cu_q[b] ..
+// cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1.  The grid covers the longest sequence
+// (n_qblocks query blocks); a work item past its own sequence's blocks exits at once.
+template <class QK, int DV, bool CAUSAL, bool VARLEN = false>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa, int n_qblocks) {
   constexpr int KPART = (QK::KBYTES + 1023) / 1024 * 1024;
   constexpr int VROWB = DV * 2;
   constexpr int STAGE = KPART + BN * VROWB;
@@ -331,13 +334,47 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qb
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int l32 = lane & 31, hl = lane >> 5;
 
-  // work item: contiguous per XCD (workgroup i runs on XCD i % 8), head-major
+  // work item (workgroup i runs on XCD i % 8); the items of one (batch, head) stay on one
+  // XCD, in order, so they share its K/V in that XCD's L2
   const int G = gridDim.x, x = blockIdx.x % 8, jx = blockIdx.x / 8;
-  const int w = x * (G / 8) + min(x, G % 8) + jx;
   const int per_head = CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks;
-  const int bh = w / per_head, it = w % per_head;
-  const int b = bh / p.Hq, h = bh % p.Hq;
-  const int kvh = h / (p.Hq / p.Hkv);
+  int bh, it;
+  if constexpr (VARLEN) {
+    // sequences differ in length: (sequence, head) pairs are dealt round-robin to the XCDs
+    // (pair bh on XCD bh % 8), so every XCD gets the same share of every sequence; the grid is
+    // padded to whole rounds of 8 pairs
+    bh = x + 8 * (jx / per_head);
+    it = jx % per_head;
+    if (bh >= pa.B * pa.Hq) return;
+  } else {
+    // equal (batch, head) pairs: each XCD takes a contiguous range of work items
+    const int w = x * (G / 8) + min(x, G % 8) + jx;
+    bh = w / per_head;
+    it = w % per_head;
+  }
+  int b = bh / pa.Hq;
+  const int h = bh % pa.Hq;
+  const int kvh = h / (pa.Hq / pa.Hkv);
+  PrefillArgs p = pa;
+  // LSE of row (b, h, qrow) at lse_off + h * lse_hs + qrow
+  size_t lse_off = (size_t)b * p.Hq * p.Sq;
+  size_t lse_hs = (size_t)p.Sq;
+  if constexpr (VARLEN) {
+    // offsets are clamped into the packed tensors, so any array contents stay in bounds
+    const int q0 = min(max(p.cu_q[b], 0), p.total_q), q1 = min(max(p.cu_q[b + 1], q0), p.total_q);
+    const int k0 = min(max(p.cu_k[b], 0), p.total_k), k1 = min(max(p.cu_k[b + 1], k0), p.total_k);
+    p.Sq = min(q1 - q0, pa.Sq);
+    p.Skv = k1 - k0;
+    n_qblocks = (p.Sq + BM - 1) / BM;
+    if (it >= (CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks)) return;
+    p.q = (const char*)p.q + (size_t)q0 * p.Hq * QK::ROWB;
+    p.o = (char*)p.o + (size_t)q0 * p.Hq * (DV * 2);
+    p.k = (const char*)p.k + (size_t)k0 * p.Hkv * QK::ROWB;
+    p.v = (const char*)p.v + (size_t)k0 * p.Hkv * (DV * 2);
+    lse_off = (size_t)q0;
+    lse_hs = (size_t)p.total_q;
+    b = 0;  // the pointers now start at the sequence
+  }
   int blk[2] = {it, it};
   int nblk = 1;
   if (CAUSAL) {
@@ -429,7 +466,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs p, int n_qb
           *(i32x2_t*)(ob + d * 2) = wv;
         }
       if (p.lse && hl == 0)
-        p.lse[((size_t)b * p.Hq + h) * p.Sq + qrow] = l_tot > 0.f ? st.m_ref * p.scale + logf(l_tot) : -INFINITY;
+        p.lse[lse_off + h * lse_hs + qrow] = l_tot > 0.f ? st.m_ref * p.scale + logf(l_tot) : -INFINITY;
     }
   }
 }
@@ -453,6 +490,22 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s) {
   } else {
     if (a.causal) prefill_kernel<QkBf16<64>, 64, true><<<grid, 256, 0, s>>>(a, nqb);
     else prefill_kernel<QkBf16<64>, 64, false><<<grid, 256, 0, s>>>(a, nqb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, int D, hipStream_t s) {
+  // a.Sq is the longest query sequence; (sequence, head) pairs padded to a multiple of 8
+  const int nqb = (a.Sq + BM - 1) / BM;
+  const int per_head = a.causal ? (nqb + 1) / 2 : nqb;
+  const int grid = (a.B * a.Hq + 7) / 8 * 8 * per_head;
+  if (grid == 0) return hipSuccess;
+  if (D == 128) {
+    if (a.causal) prefill_kernel<QkBf16<128>, 128, true, true><<<grid, 256, 0, s>>>(a, nqb);
+    else prefill_kernel<QkBf16<128>, 128, false, true><<<grid, 256, 0, s>>>(a, nqb);
+  } else {
+    if (a.causal) prefill_kernel<QkBf16<64>, 64, true, true><<<grid, 256, 0, s>>>(a, nqb);
+    else prefill_kernel<QkBf16<64>, 64, false, true><<<grid, 256, 0, s>>>(a, nqb);
   }
   return hipGetLastError();
 }

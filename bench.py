@@ -26,6 +26,7 @@ METRIC = "prefill attn TFLOP/s (% MFMA peak); decode KV GB/s (% HBM peak)"
 PEAK = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "hbm": 8000.0}   # TFLOP/s, GB/s
 # What the HIP events around one call time: the whole call (decode = split kernel + combine).
 KERNELS = {"prefill": "prefill kernel", "mla_prefill": "prefill kernel (MLA policy)",
+           "prefill_varlen": "prefill kernel (ragged batch)", "merge": "merge_kernel",
            "decode": "gqa_decode_split + combine_kernel (one call)",
            "mla_decode": "mla_decode_split + combine_kernel (one call)",
            "quantize": "quantize_rows_kernel"}
@@ -44,6 +45,14 @@ def algorithmic_work(w, lens=None):
         esz = 4 if w.dtype == "f32" else 2
         byts = esz * w.B * (w.Sq * w.Hq * (w.D + w.Dv) + w.Skv * w.Hkv * (w.D + w.Dv))
         return flops, byts
+    if w.kind == "prefill_varlen":
+        # each sequence is a causal prefill with its own length; lens = the sequence lengths
+        pairs = sum(int(n) * (int(n) + 1) // 2 for n in lens) if w.causal else sum(int(n) ** 2 for n in lens)
+        toks = int(sum(lens))
+        return 2 * (w.D + w.Dv) * pairs * w.Hq, 2 * toks * (w.Hq + w.Hkv) * (w.D + w.Dv)
+    if w.kind == "merge":
+        rows = w.B * w.Sq * w.Hq
+        return 0, rows * (3 * w.D * 2 + 3 * 4)   # two bf16 parts in, one out; two LSEs in, one out
     if w.kind == "decode":
         sl = int(sum(lens))
         flops = 2 * w.Hq * (w.D + w.Dv) * sl
@@ -106,6 +115,22 @@ def setup(w):
             q, k, v = (torch.from_numpy(d[n]).cuda() for n in ("q", "k", "v"))
         o = torch.empty_like(q)
         return (lambda i: fa.prefill(q, k, v, causal=w.causal, scale=w.scale, out=o)), None, (q, k, v, o)
+    if w.kind == "prefill_varlen":
+        from workloads import make_prefill_varlen
+        d = make_prefill_varlen(w)
+        q, k, v = bf16(d["q"]), bf16(d["k"]), bf16(d["v"])
+        cu = torch.from_numpy(d["cu"]).cuda()
+        o = torch.empty_like(q)
+        mx = int(d["lens"].max())
+        return (lambda i: fa.prefill_varlen(q, k, v, cu, cu, mx, causal=w.causal, scale=w.scale, out=o)), \
+            d["lens"], (q, k, v, cu, o)
+    if w.kind == "merge":
+        from workloads import make_merge
+        d = make_merge(w)
+        oa, ob = bf16(d["o_a"]), bf16(d["o_b"])
+        la, lb = torch.from_numpy(d["lse_a"]).cuda(), torch.from_numpy(d["lse_b"]).cuda()
+        o, lse = torch.empty_like(oa), torch.empty_like(la)
+        return (lambda i: fa.merge(oa, la, ob, lb, out=o, out_lse=lse)), None, (oa, ob, la, lb, o, lse)
     if w.kind == "decode":
         d = make_decode(w)
         q, kv_lens = bf16(d["q"]), torch.from_numpy(d["kv_lens"]).cuda()
@@ -195,6 +220,42 @@ def cpu_baseline(w, lens, budget_s: float):
         what = f"{n} (batch, head) pairs x all {w.Sq} query rows"
         return {"value": done_work / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
                 "sample": what, "seconds": round(t_used, 2)}
+    if w.kind == "prefill_varlen":
+        from workloads import make_prefill_varlen
+        d = make_prefill_varlen(w)
+        cu = d["cu"]
+        done = 0.0
+        for b in range(w.B):
+            for h in range(w.Hq):
+                s0, s1 = int(cu[b]), int(cu[b + 1])
+                sl = lambda x: oracle.bf16_to_f64(x[s0:s1, h:h + 1])[None]
+                args = (sl(d["q"]), sl(d["k"]), sl(d["v"]))
+                t0 = time.perf_counter()
+                for r0 in range(0, s1 - s0, 1024):
+                    oracle.prefill_rows(*args, w.scale, w.causal, 0, 0, np.arange(r0, min(s1 - s0, r0 + 1024)))
+                t_used += time.perf_counter() - t0
+                n += 1
+                f, _ = algorithmic_work(w.with_(Hq=1, Hkv=1), lens=[s1 - s0])
+                done += f
+                if t_used >= budget_s:
+                    break
+            if t_used >= budget_s:
+                break
+        return {"value": done / t_used / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                "sample": f"{n} (sequence, head) pairs x all their query rows", "seconds": round(t_used, 2)}
+    if w.kind == "merge":
+        from workloads import make_merge
+        d = make_merge(w.with_(B=1, Sq=min(w.Sq, 512)))
+        args = (oracle.bf16_to_f64(d["o_a"]), d["lse_a"].astype(np.float64), oracle.bf16_to_f64(d["o_b"]),
+                d["lse_b"].astype(np.float64))
+        while t_used < budget_s and n < 200:
+            t0 = time.perf_counter()
+            oracle.merge_states(*args)
+            t_used += time.perf_counter() - t0
+            n += 1
+        _, byts = algorithmic_work(w.with_(B=1, Sq=d["o_a"].shape[1]))
+        return {"value": n * byts / t_used / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                "sample": f"{n} passes over {d['o_a'].shape[1]} tokens x {w.Hq} heads", "seconds": round(t_used, 2)}
     if w.kind == "quantize":
         from workloads import make_quantize
         d = make_quantize(w, tokens=min(w.Sq, 256))["x"]
@@ -320,7 +381,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
 
-    if w.kind in ("prefill", "mla_prefill"):
+    if w.kind in ("prefill", "prefill_varlen", "mla_prefill"):
         if w.kind == "mla_prefill":
             f_fp8, f_bf16 = flops
             total = f_fp8 + f_bf16
@@ -355,13 +416,16 @@ def main():
            "Dv": w.Dv, "causal": w.causal, "parallelism": "none (1 GPU)"}
     if w.kind == "mla_prefill":
         cfg.update({"Dn": w.Dn, "Dr": w.Dr, "Hr": w.Hr})
-    if lens is not None:
+    if lens is not None and w.kind == "prefill_varlen":
+        cfg.update({"seq_lens": [int(x) for x in lens], "total_tokens": int(sum(lens)),
+                    "len_range": [w.len_lo, w.len_hi]})
+    elif lens is not None:
         cfg.update({"sum_kv_len": int(sum(lens)), "len_range": [w.len_lo, w.len_hi]})
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "spinup_s": args.spinup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32->e4m3" if w.kind == "quantize" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16",
+        "dtype": "f32->e4m3" if w.kind == "quantize" else "bf16 (fp32 LSE)" if w.kind == "merge" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16",
                                                            "fp8": "e4m3 cache, bf16 q/o"}[w.dtype],
         "data": "synthetic (seeded N(0,1), see workloads/)", "config": cfg, "roofline": roof,
         "kernel_ms": round(launch_ms, 4), "algorithmic": {"flops": flops if not isinstance(flops, tuple) else list(flops),

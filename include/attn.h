@@ -77,6 +77,44 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
                      float softmax_scale, hipStream_t stream);
 
 /*
+ * Ragged-batch prefill over packed sequences (KVPipelineGeneric page: S = Q.K' then
+ * O += P.V over pipelined K/V tiles, here per sequence).  Sequence b owns query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and key rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1 of k and v; each is an independent attention with its own causal
+ * alignment (bottom-right: a query chunk of Sq_b rows after a cached prefix sees keys
+ * j <= i + (Skv_b - Sq_b), so chunked prefill over a contiguous prefix is one call).
+ *   q, o [total_q, Hq, D]; k, v [total_k, Hkv, D]: bf16 (dtype must be ATTN_BF16).
+ *   cu_seqlens_q, cu_seqlens_k: DEVICE int32 [B+1], non-decreasing from 0, last entry
+ *   <= total_q (resp. total_k); every query length <= max_seqlen_q.  The kernel clamps
+ *   the offsets into [0, total], so inconsistent arrays give unspecified values but no
+ *   access outside the tensors; rows of o outside every sequence are not written.
+ *   lse: NULL or fp32 [Hq, total_q].
+ *   Supported: D in {64, 128}; Hq % Hkv == 0.
+ */
+int attn_prefill_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int dtype, int B,
+                            int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int D, int causal,
+                            float softmax_scale, hipStream_t stream);
+
+/*
+ * Merge of two partial attention results of the same query rows over disjoint key sets
+ * (the per-row correction of the running softmax, MLASmemStorage page correction_smem,
+ * applied to two finished parts):
+ *   M = max(lse_a, lse_b), w = exp(lse - M),
+ *   o = (w_a o_a + w_b o_b) / (w_a + w_b),  lse = M + ln(w_a + w_b);
+ * both parts empty (lse = -inf) gives o = 0, lse = -inf.  Used to finish a query chunk
+ * from a prefill over its cached prefix (non-causal) and one over the chunk (causal).
+ *   o_a, o_b, o [B, S, H, D] of `dtype` (ATTN_BF16 or ATTN_F32); lse_a, lse_b [B, H, S]
+ *   fp32 (the layout attn_prefill_fwd writes; a ragged batch is B = 1, S = total_q);
+ *   lse: NULL or fp32 [B, H, S].  o may be o_a or o_b and lse may be lse_a or lse_b
+ *   (in place); other overlaps are not allowed.
+ *   Supported: D * element size a multiple of 16 bytes, D * element size / 16 a power of
+ *   two <= 64 (bf16 D in {8, ..., 512}, fp32 D in {4, ..., 256}).
+ */
+int attn_merge_fwd(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o,
+                   float* lse, int dtype, int B, int S, int H, int D, hipStream_t stream);
+
+/*
  * Decode (token generation; AMD buffers page, token_gen variant of the K/V buffers):
  * one query token per sequence attends to keys [0, kv_lens[b]) of its cache.
  *   q [B,Hq,D] bf16; o [B,Hq,D] bf16;

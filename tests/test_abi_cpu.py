@@ -154,3 +154,44 @@ def test_quantize_validation(lib):
     assert q(x=NUL) == ENULL
     assert q(c=NUL) == ENULL
     assert q(s=NUL) == ENULL
+
+
+def varlen(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, cq=FAKE, ck=FAKE, dtype=1, B=3, Tq=300, Tk=400, maxq=200, Hq=4,
+           Hkv=2, D=128, causal=1, scale=0.1):
+    return lib.attn_prefill_varlen_fwd(q, k, v, o, NUL, cq, ck, dtype, B, Tq, Tk, maxq, Hq, Hkv, D, causal, scale, S)
+
+
+def test_prefill_varlen_validation(lib):
+    assert varlen(lib, dtype=0) == EDTYPE           # ragged batches are bf16 only
+    assert varlen(lib, dtype=2) == EDTYPE
+    assert varlen(lib, B=-1) == ESHAPE
+    assert varlen(lib, Tq=-1) == ESHAPE
+    assert varlen(lib, maxq=-1) == ESHAPE
+    assert varlen(lib, Hq=3) == ESHAPE
+    assert varlen(lib, D=96) == EUNSUP
+    assert varlen(lib, scale=0.0) == ESCALE
+    assert varlen(lib, cq=NUL) == ENULL
+    assert varlen(lib, ck=NUL) == ENULL
+    assert varlen(lib, k=NUL) == ENULL
+    assert varlen(lib, q=NUL) == ENULL
+    assert varlen(lib, q=NUL, k=NUL, v=NUL, o=NUL, cq=NUL, ck=NUL, B=0) == OK
+    assert varlen(lib, q=NUL, k=NUL, v=NUL, o=NUL, cq=NUL, ck=NUL, Tq=0) == OK
+    assert varlen(lib, q=NUL, k=NUL, v=NUL, o=NUL, cq=NUL, ck=NUL, maxq=0) == OK
+
+
+def merge(lib, oa=FAKE, la=FAKE, ob=FAKE, lb=FAKE, o=FAKE, dtype=1, B=2, S_=16, H=4, D=128):
+    return lib.attn_merge_fwd(oa, la, ob, lb, o, NUL, dtype, B, S_, H, D, S)
+
+
+def test_merge_validation(lib):
+    assert merge(lib, dtype=2) == EDTYPE
+    assert merge(lib, B=-1) == ESHAPE
+    assert merge(lib, H=0) == ESHAPE
+    assert merge(lib, D=100) == EUNSUP            # 200 bytes: not whole 16-byte chunks
+    assert merge(lib, D=96) == EUNSUP             # 12 chunks: not a power of two
+    assert merge(lib, D=1024) == EUNSUP           # 128 chunks per row
+    assert merge(lib, dtype=0, D=512) == EUNSUP   # fp32: 128 chunks per row
+    assert merge(lib, oa=NUL) == ENULL
+    assert merge(lib, lb=NUL) == ENULL
+    assert merge(lib, o=NUL) == ENULL
+    assert merge(lib, oa=NUL, la=NUL, ob=NUL, lb=NUL, o=NUL, S_=0) == OK

@@ -17,11 +17,14 @@ from .gen import (
     make_mla_decode,
     make_quantize,
     decode_lengths,
+    varlen_lengths,
+    make_prefill_varlen,
+    make_merge,
 )
 
 __all__ = [
     "bf16_bits", "bf16_bits_to_f32", "e4m3_encode", "quantize_rows_e4m3",
     "WORKLOADS", "Workload", "workload",
     "normal_f32", "make_prefill", "make_decode", "make_mla_prefill", "make_mla_decode", "make_quantize",
-    "decode_lengths",
+    "decode_lengths", "varlen_lengths", "make_prefill_varlen", "make_merge",
 ]

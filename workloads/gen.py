@@ -26,6 +26,7 @@ CHUNK = 256
 
 # tensor ids of the streams
 T_Q, T_K, T_V, T_QNOPE, T_KNOPE, T_QROPE, T_KROPE, T_KV = 1, 2, 3, 4, 5, 6, 7, 8
+T_LSE_A, T_LSE_B = 9, 10
 
 
 def _threads() -> int:
@@ -99,6 +100,35 @@ def decode_lengths(w: Workload) -> np.ndarray:
         return np.full(w.B, w.len_lo, np.int32)
     rng = np.random.Generator(np.random.PCG64([w.seed, 1000]))
     return rng.integers(w.len_lo, w.len_hi + 1, size=w.B).astype(np.int32)
+
+
+def varlen_lengths(w: Workload) -> np.ndarray:
+    """Ragged prefill: per-sequence token counts, int32 [B], uniform on [len_lo, len_hi] (the
+    same stream as the decode lengths)."""
+    return decode_lengths(w)
+
+
+def make_prefill_varlen(w: Workload) -> dict:
+    """Ragged prefill: packed q [T, Hq, D], k/v [T, Hkv, D] (bf16 bits) for the sequences of
+    varlen_lengths(w) laid end to end (each sequence's keys are its own tokens), and the
+    offsets cu [B+1]."""
+    lens = varlen_lengths(w)
+    T = int(lens.sum())
+    d = make_prefill(w.with_(B=1, Sq=T, Skv=T))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return {"q": d["q"][0], "k": d["k"][0], "v": d["v"][0], "cu": cu, "lens": lens}
+
+
+def make_merge(w: Workload) -> dict:
+    """Two partial states: o_a, o_b [B, S, H, D] (bf16 bits or fp32) and lse_a, lse_b [B, H, S]
+    fp32, all i.i.d. N(0, 1)."""
+    d = make_prefill(w.with_(Skv=w.Sq, Hkv=w.Hq))
+    la = np.zeros((w.B, w.Hq, w.Sq), np.float32)
+    lb = np.zeros((w.B, w.Hq, w.Sq), np.float32)
+    for b in range(w.B):
+        la[b] = normal_f32(w.seed, T_LSE_A, b, 0, (w.Hq, w.Sq))
+        lb[b] = normal_f32(w.seed, T_LSE_B, b, 0, (w.Hq, w.Sq))
+    return {"o_a": d["q"], "o_b": d["k"], "lse_a": la, "lse_b": lb}
 
 
 def make_decode(w: Workload, batches=None, lens=None) -> dict:

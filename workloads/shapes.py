@@ -12,7 +12,7 @@ from dataclasses import dataclass, replace
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "prefill" | "decode" | "mla_prefill" | "mla_decode" | "quantize"
+    kind: str                 # "prefill" | "prefill_varlen" | "merge" | "decode" | "mla_prefill" | "mla_decode" | "quantize"
     seed: int
     dtype: str                # storage dtype of q/k/v: "f32" | "bf16" | "fp8+bf16" | "fp8" (decode cache)
     B: int
@@ -26,7 +26,7 @@ class Workload:
     Dn: int = 0               # MLA prefill nope depth
     Dr: int = 0               # MLA prefill rope depth
     Hr: int = 1               # MLA prefill k_rope heads (1 = shared by every head)
-    len_lo: int = 0           # decode: per-sequence lengths uniform on [len_lo, len_hi]
+    len_lo: int = 0           # decode (KV) and ragged prefill: per-sequence lengths uniform on [len_lo, len_hi]
     len_hi: int = 0
     scale: float = 0.0
     notes: str = ""
@@ -72,6 +72,17 @@ WORKLOADS = {
         name="mla_prefill_fp8_causal_b1_h128_s8192", kind="mla_prefill", seed=5, dtype="fp8+bf16",
         B=1, Hq=128, Hkv=128, Sq=8192, Skv=8192, D=192, Dv=128, causal=True, Dn=128, Dr=64, Hr=1,
         scale=1.0 / 192 ** 0.5),
+    # Ragged-batch causal prefill: 8 packed sequences with lengths uniform on [512, 3584]
+    # (16384 tokens on average, the token count of the B4 S4096 prefill), 32 heads, D 128, bf16.
+    "mha_prefill_varlen_causal_bf16_b8_len512to3584_h32_d128": Workload(
+        name="mha_prefill_varlen_causal_bf16_b8_len512to3584_h32_d128", kind="prefill_varlen", seed=6,
+        dtype="bf16", B=8, Hq=32, Hkv=32, D=128, Dv=128, causal=True, len_lo=512, len_hi=3584,
+        scale=1.0 / 128 ** 0.5),
+    # Merge of two partial attention results of the B4 S4096 H32 D128 prefill's shape (bf16 outputs,
+    # fp32 LSEs), e.g. a cached-prefix part and a chunk part.
+    "merge_bf16_b4_s4096_h32_d128": Workload(
+        name="merge_bf16_b4_s4096_h32_d128", kind="merge", seed=7, dtype="bf16",
+        B=4, Hq=32, Hkv=32, Sq=4096, Skv=4096, D=128, Dv=128),
     # Per-token e4m3 quantisation of the MLA prefill q_nope originals: 8192 tokens x 128 heads
     # rows of 128 fp32 values (the same draws the MLA prefill workload quantises).
     "quantize_e4m3_rows_b1_s8192_h128_d128": Workload(
