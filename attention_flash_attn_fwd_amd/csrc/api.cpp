@@ -124,7 +124,7 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
   if (!q || !o || !kv_lens || (max_kv_len > 0 && (!k_cache || !v_cache))) return ATTN_ERR_NULL;
   if (fp8 && max_kv_len > 0 && (!k_scale || !v_scale)) return ATTN_ERR_NULL;
   const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);
-  if (B > 65535 || p.n_split > 65535 || elems({p.n_split, Hkv, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (B > 65535 || p.n_split > 65535 || elems({p.n_split, Hkv, (B + 7) / 8 * 8}) > INT32_MAX) return ATTN_ERR_SHAPE;
   if (elems({B, Hq, D}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
   const size_t need = fa::decode_workspace_bytes(B, Hq, D, p.n_split);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;

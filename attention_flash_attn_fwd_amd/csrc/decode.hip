@@ -20,26 +20,45 @@ namespace {
 
 constexpr int TK = 32;  // keys per tile
 
-// ------------------------------------------------------------------------------------
-// GQA decode split: one wave per workgroup = one split of one (batch, kv head).  K goes
-// from global memory straight into the MFMA A-operand registers (buffer loads; rows past
-// the sequence read as zero), two register slots deep; only V, which must be read
-// transposed, is staged in LDS by direct loads (two stages, 16 KiB per wave).  The small
-// LDS footprint lets ~10 waves share a CU, which keeps enough bytes in flight to stream
-// the cache at HBM rate.
+// Work item of a GQA split kernel (one wave = one split of one (batch, kv head)).  The grid
+// is 1-D; workgroup i runs on XCD i % 8.  The Hkv waves of one (split, batch) pair take
+// consecutive positions on one XCD, so each token's kv-head rows -- adjacent in the cache --
+// are read together through that XCD's L2 (one 128-byte e4m3 row per head would otherwise
+// be fetched by eight XCDs apart).  Pair (split, b) runs on XCD (split + b) % 8, splits in
+// order: every sequence's splits spread over all XCDs and early (full) splits go first.
+// Batch entries are padded to a multiple of 8; items past B exit.
+__device__ __forceinline__ bool gqa_item(const DecodeArgs& a, int& kvh, int& split, int& b) {
+  const int i = blockIdx.x, x = i & 7, j = i >> 3;
+  kvh = j % a.Hkv;
+  const int gi = j / a.Hkv, nb8 = (a.B + 7) / 8;
+  split = gi / nb8;
+  b = ((x - split) & 7) + 8 * (gi % nb8);
+  return b < a.B;
+}
 
+// ------------------------------------------------------------------------------------
+// GQA decode split: one wave per workgroup = one split of one (batch, kv head).  K and V
+// tiles of 32 keys go HBM -> LDS by direct loads into a private ring of GQA_NS stages (no
+// barriers: the wave is alone in its workgroup).  Every LDS read of a tile is an asm block
+// that waits for itself (lds_* in device.h), so no instruction the compiler sees consumes
+// a load result inside the loop: the only vector-memory waits are the explicit ones, and
+// GQA_NS - 1 tiles stay in flight while a tile is computed.
+
+constexpr int GQA_NS = 3;  // LDS stages per wave
+
+// LDS byte offsets of a 32-key tile of 256-byte rows (bf16 D = 128), 16-byte chunks
+// XOR-permuted by swz16: the direct copy (lane -> row 4i + lane/16), the S^T A operand
+// (row 16kb + l16, chunk 4cc + g) and the transposed V reads (see below).
 template <int G>
 __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
-  constexpr int D = 128, ROWB = 256, VTILE = TK * ROWB;
-  constexpr int KOPS = 8, VOPS = VTILE / 1024;  // vector-memory instructions per tile
-  // one LDS object per stage, selected at compile time (see the prefill kernel)
-  __shared__ __attribute__((aligned(1024))) char v0_raw[VTILE];
-  __shared__ __attribute__((aligned(1024))) char v1_raw[VTILE];
-  FA_LDS char* const vst[2] = {(FA_LDS char*)v0_raw, (FA_LDS char*)v1_raw};
+  constexpr int D = 128, ROWB = 256, TILE = TK * ROWB;  // 8 KiB per K or V tile
+  constexpr int STAGE = 2 * TILE;                       // K tile | V tile
+  constexpr int OPS = STAGE / 1024;                     // direct copies per tile (16)
+  __shared__ __attribute__((aligned(1024))) char ring_raw[GQA_NS * STAGE];
+  FA_LDS char* const ring = (FA_LDS char*)ring_raw;
 
-  // kv head fastest: the workgroups of one (batch, split) run together and read each
-  // token's kv heads, which are adjacent in the cache, as one contiguous stretch
-  const int kvh = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  int kvh, split, b;
+  if (!gqa_item(a, kvh, split, b)) return;
   const int L = min(max(a.kv_lens[b], 0), a.max_len);
   const int start = split * a.chunk;
   if (start >= L) return;
@@ -64,47 +83,53 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
   }
   const char* kbase = (const char*)a.k + ((size_t)b * a.max_len * a.Hkv + kvh) * ROWB;
   const char* vbase = (const char*)a.v + ((size_t)b * a.max_len * a.Hkv + kvh) * ROWB;
-  // K A operand of key block kb: row 16kb + l16, head-dim chunk 4cc + g
-  const uint32_t koff0 = l16 * rstride + g * 16, koff1 = (16 + l16) * rstride + g * 16;
-  // V copy: LDS row 4i + g holds key row 4i + g with 16-byte chunks XOR-permuted
-  uint32_t voff[VOPS];
+  // direct copy: LDS row 4i + g holds key row 4i + g with 16-byte chunks XOR-permuted
+  uint32_t coff[TILE / 1024];
 #pragma unroll
-  for (int i = 0; i < VOPS; i++) {
+  for (int i = 0; i < TILE / 1024; i++) {
     const uint32_t row = 4 * i + g;
-    voff[i] = row * rstride + ((l16 ^ swz16(row)) << 4);
+    coff[i] = row * rstride + ((l16 ^ swz16(row)) << 4);
   }
+  // S^T A operand of key block kb, step cc: row 16kb + l16, chunk 4cc + g
+  uint32_t ka[8];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) {
+      const uint32_t row = 16 * kb + l16;
+      ka[4 * kb + cc] = row * ROWB + (((4 * cc + g) ^ swz16(row)) << 4);
+    }
   // transposing V reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4) .. +3.  The column
   // slab of block db is chunk pair db: swizzled to pair db ^ (swz >> 1), chunk (l16%4)/2 of
   // the pair flipped by swz & 1.
-  uint32_t vrow[2], vpair[2];
+  uint32_t va[D / 16][2];
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     const uint32_t row = 16 * u + 4 * g + (l16 >> 2), sw = swz16(row);
-    vrow[u] = row * ROWB + (((((l16 & 3) >> 1) ^ (sw & 1))) << 4) + ((l16 & 1) << 3);
-    vpair[u] = sw >> 1;
+    const uint32_t base = TILE + row * ROWB + (((((l16 & 3) >> 1) ^ (sw & 1))) << 4) + ((l16 & 1) << 3);
+#pragma unroll
+    for (int db = 0; db < D / 16; db++) va[db][u] = base + ((db ^ (sw >> 1)) << 5);
   }
 
-  i32x4_t kf[2][2][D / 32];
-  auto issue_k = [&](int t, i32x4_t (&dst)[2][D / 32]) {
-    const int key0 = start + t * TK;
-    const auto r = make_rsrc(kbase + (size_t)key0 * rstride, (uint32_t)(end - key0) * rstride);
-#pragma unroll
-    for (int cc = 0; cc < D / 32; cc++) {
-      dst[0][cc] = __builtin_amdgcn_raw_buffer_load_b128(r, koff0 + cc * 64, 0, 0);
-      dst[1][cc] = __builtin_amdgcn_raw_buffer_load_b128(r, koff1 + cc * 64, 0, 0);
-    }
-  };
-  auto issue_v = [&](int t, FA_LDS char* dst) {
+  // tile t -> stage t % GQA_NS; rows past the sequence repeat its last row (masked below)
+  auto issue = [&](int t) {
     const int key0 = start + t * TK, valid = min(TK, end - key0);
-    const auto r = make_rsrc(vbase + (size_t)key0 * rstride, (uint32_t)(valid - 1) * rstride + ROWB);
+    FA_LDS char* dst = ring + (t % GQA_NS) * STAGE;
+    const uint32_t bytes = (uint32_t)(valid - 1) * rstride + ROWB;
+    const auto rk = make_rsrc(kbase + (size_t)key0 * rstride, bytes);
+    const auto rv = make_rsrc(vbase + (size_t)key0 * rstride, bytes);
     if (valid == TK) {
 #pragma unroll
-      for (int i = 0; i < VOPS; i++) dma16_buf(r, dst + i * 1024, voff[i]);
+      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rk, dst + i * 1024, coff[i]);
+#pragma unroll
+      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rv, dst + TILE + i * 1024, coff[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < VOPS; i++) {
+      for (int i = 0; i < TILE / 1024; i++) {
         const uint32_t row = 4 * i + g, rc = min(row, (uint32_t)(valid - 1));
-        dma16_buf(r, dst + i * 1024, rc * rstride + ((l16 ^ swz16(row)) << 4));
+        const uint32_t off = rc * rstride + ((l16 ^ swz16(row)) << 4);
+        dma16_buf(rk, dst + i * 1024, off);
+        dma16_buf(rv, dst + TILE + i * 1024, off);
       }
     }
   };
@@ -114,19 +139,32 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 #pragma unroll
   for (int d = 0; d < D / 16; d++) o[d] = f32x4_t{};
 
-  // tile t: K(t) in kf[t & 1] (issued two tiles earlier), V(t) in vst[t & 1] (one tile
-  // earlier).  Issue order per tile: V(t+1), then K(t+2) once K(t) has been consumed.
-  auto tile = [&](auto SLOT, int t) {
-    constexpr int sl = decltype(SLOT)::value;
-    if (t + 1 < n_tiles) issue_v(t + 1, vst[sl ^ 1]);
+  // prologue: tiles 0 .. GQA_NS-2.  Every tile then issues tile t + GQA_NS - 1 (past the
+  // end, a repeat of the last tile: an L2 hit, never read), so exactly GQA_NS - 1 tiles
+  // of copies are younger than tile t's and the wait count is the same on every path.
+#pragma unroll
+  for (int p = 0; p < GQA_NS - 1; p++) issue(min(p, n_tiles - 1));
+  for (int t = 0; t < n_tiles; t++) {
+    // the stage refilled here held tile t - 1, whose reads completed in their asm blocks
+    issue(min(t + GQA_NS - 1, n_tiles - 1));
+    wait_vmcnt<(GQA_NS - 1) * OPS>();
+    asm volatile("" ::: "memory");
+    const uint32_t st = lds_addr(ring) + (t % GQA_NS) * STAGE;
+
+    i32x4_t kf[8];
+    {
+      uint32_t ad[8];
+#pragma unroll
+      for (int i = 0; i < 8; i++) ad[i] = st + ka[i];
+      lds_b128_x8(kf, ad);
+    }
     f32x4_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
       s[kb] = f32x4_t{};
 #pragma unroll
-      for (int cc = 0; cc < D / 32; cc++) s[kb] = mfma16x16x32_bf16(kf[sl][kb][cc], qf[cc], s[kb]);
+      for (int cc = 0; cc < D / 32; cc++) s[kb] = mfma16x16x32_bf16(kf[4 * kb + cc], qf[cc], s[kb]);
     }
-    if (t + 2 < n_tiles) issue_k(t + 2, kf[sl]);
     const int key0 = start + t * TK;
     if (key0 + TK > end) {
 #pragma unroll
@@ -156,28 +194,22 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
     const i32x4_t pb = {pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
 #pragma unroll
     for (int i = 0; i < 4; i++) l = dot2_bf16(pb[i], kBf16PairOne, l);
-    // V(t) must have landed: later vector-memory ops are K(t+1), V(t+1), K(t+2)
-    if (t + 2 < n_tiles) wait_vmcnt<2 * KOPS + VOPS>();
-    else if (t + 1 < n_tiles) wait_vmcnt<KOPS + VOPS>();
-    else wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    const FA_LDS char* vt = vst[sl];
 #pragma unroll
-    for (int db = 0; db < D / 16; db++) {
-      const i32x2_t lo = lds_tr16(vt + vrow[0] + ((db ^ vpair[0]) << 5));
-      const i32x2_t hi = lds_tr16(vt + vrow[1] + ((db ^ vpair[1]) << 5));
-      o[db] = mfma16x16x32_bf16(cat(lo, hi), pb, o[db]);
+    for (int half = 0; half < 2; half++) {
+      uint32_t ad[8];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        ad[2 * j] = st + va[4 * half + j][0];
+        ad[2 * j + 1] = st + va[4 * half + j][1];
+      }
+      i32x2_t vr[8];
+      lds_tr16_x8(vr, ad);
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        o[4 * half + j] = mfma16x16x32_bf16(cat(vr[2 * j], vr[2 * j + 1]), pb, o[4 * half + j]);
     }
-  };
-
-  issue_k(0, kf[0]);
-  issue_v(0, vst[0]);
-  if (1 < n_tiles) issue_k(1, kf[1]);
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 >= n_tiles) break;
-    tile(std::integral_constant<int, 1>{}, t + 1);
   }
+  wait_vmcnt<0>();  // the repeat copies past the end land before the LDS is released
 
   const float l_tot = xor32_sum(xor16_sum(l));
   if (l16 < G) {
@@ -196,27 +228,26 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 // ------------------------------------------------------------------------------------
 // GQA decode split over an e4m3 cache with per-token scales (k_scale, v_scale per key row
 // and kv head).  Same structure as the bf16 kernel, at half the bytes per key:
-//  * K (128-byte rows) goes straight into registers; the contraction order is permuted so
+//  * K codes (128-byte rows) go through the LDS ring; the contraction order is permuted so
 //    that a lane's four K fragments are one contiguous 32-byte run of its key row (step cc,
 //    lane group g, element i covers head dim 32g + 8cc + i; Q^T uses the same order), and
 //    e4m3 -> bf16 is exact, so S^T = K_code.Q^T runs on the bf16 matrix cores and the key
 //    scale multiplies S afterwards;
-//  * V codes are staged in LDS by direct loads with the key and value scales of the tile,
-//    read transposed one byte wide (ds_read_b64_tr_b8: 8 keys of one column per lane, one
-//    read per product instead of two), converted exactly, and the value scale is folded
-//    into P: O += (P . v_scale) V_code.
+//  * V codes are read transposed one byte wide (ds_read_b64_tr_b8: 8 keys of one column per
+//    lane, one read per product instead of two), converted exactly, and the value scale is
+//    folded into P: O += (P . v_scale) V_code.
 
 template <int G>
 __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
-  constexpr int D = 128, ROWB = 128, VT = TK * ROWB;
-  constexpr int SCB = 256;                         // one scale DMA: 64 lanes x 4 bytes
-  constexpr int STAGE = VT + 2 * SCB;              // V codes | k_scale | v_scale
-  constexpr int KOPS = 4, VOPS = VT / 1024 + 2;    // vector-memory instructions per tile
-  __shared__ __attribute__((aligned(1024))) char v0_raw[STAGE];
-  __shared__ __attribute__((aligned(1024))) char v1_raw[STAGE];
-  FA_LDS char* const vst[2] = {(FA_LDS char*)v0_raw, (FA_LDS char*)v1_raw};
+  constexpr int D = 128, ROWB = 128, TILE = TK * ROWB;  // 4 KiB per K or V tile
+  constexpr int SCB = 256;                              // one scale copy: 64 lanes x 4 bytes
+  constexpr int STAGE = 2 * TILE + 2 * SCB;             // K codes | V codes | k_scale | v_scale
+  constexpr int OPS = 2 * TILE / 1024 + 2;              // direct copies per tile (10)
+  __shared__ __attribute__((aligned(1024))) char ring_raw[GQA_NS * STAGE];
+  FA_LDS char* const ring = (FA_LDS char*)ring_raw;
 
-  const int kvh = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  int kvh, split, b;
+  if (!gqa_item(a, kvh, split, b)) return;
   const int L = min(max(a.kv_lens[b], 0), a.max_len);
   const int start = split * a.chunk;
   if (start >= L) return;
@@ -245,55 +276,62 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
   const char* vbase = (const char*)a.v + row0 * ROWB;
   const float* ksbase = a.k_scale + row0;
   const float* vsbase = a.v_scale + row0;
-  // K: key rows 16kb + l16, bytes 32g .. 32g + 31 as two 16-byte loads
-  const uint32_t koff0 = l16 * rstride + 32 * g, koff1 = (16 + l16) * rstride + 32 * g;
-  // V copy: LDS row 8i + lane/8 holds key row 8i + lane/8 with its 16-byte chunks
-  // XOR-permuted by swz_fp8v
-  uint32_t voff[VT / 1024];
+  // direct copies: LDS row 8i + lane/8 holds key row 8i + lane/8, its 16-byte chunks
+  // XOR-permuted by swz_half (K) and swz_fp8v (V)
+  uint32_t kcoff[TILE / 1024], vcoff[TILE / 1024];
 #pragma unroll
-  for (int i = 0; i < VT / 1024; i++) {
+  for (int i = 0; i < TILE / 1024; i++) {
     const uint32_t row = 8 * i + lane / 8;
-    voff[i] = row * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4);
+    kcoff[i] = row * rstride + (((lane & 7) ^ swz_half(row)) << 4);
+    vcoff[i] = row * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4);
   }
+  // K fragments: key row 16kb + l16, bytes 32g + 16hh .. +15 (chunk 2g + hh)
+  uint32_t ka[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; kb++)
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {
+      const uint32_t row = 16 * kb + l16;
+      ka[2 * kb + hh] = row * ROWB + (((2 * g + hh) ^ swz_half(row)) << 4);
+    }
   // transposing V reads: lane 2e + h of group g reads key row R = 16(e/4) + 4g + e%4 at
   // byte 8h of column chunk db, so output byte e of lane l is column 16db + l%16 of key R --
   // the key order in which P^T is packed below
-  uint32_t vrd, vsw;
+  uint32_t va[D / 16];
   {
     const uint32_t e = (lane & 15) >> 1, h = lane & 1;
     const uint32_t row = 16 * (e >> 2) + 4 * g + (e & 3);
-    vrd = row * ROWB + 8 * h;
-    vsw = swz_fp8v(row);
-  }
-
-  i32x4_t kf[2][2][2];  // [slot][kb][16-byte half]: 32 e4m3 K codes per key row
-  auto issue_k = [&](int t, i32x4_t (&dst)[2][2]) {
-    const int key0 = start + t * TK;
-    const auto r = make_rsrc(kbase + (size_t)key0 * rstride, (uint32_t)(end - key0) * rstride);
 #pragma unroll
-    for (int hh = 0; hh < 2; hh++) {
-      dst[0][hh] = __builtin_amdgcn_raw_buffer_load_b128(r, koff0 + 16 * hh, 0, 0);
-      dst[1][hh] = __builtin_amdgcn_raw_buffer_load_b128(r, koff1 + 16 * hh, 0, 0);
-    }
-  };
-  auto issue_v = [&](int t, FA_LDS char* dst) {
+    for (int db = 0; db < D / 16; db++) va[db] = TILE + row * ROWB + 8 * h + ((db ^ swz_fp8v(row)) << 4);
+  }
+  // scales of the tile's keys: register v of block kb holds key 16kb + 4g + v
+  const uint32_t g16 = 16u * g;
+  const uint32_t sa[4] = {2 * TILE + g16, 2 * TILE + 64 + g16, 2 * TILE + SCB + g16, 2 * TILE + SCB + 64 + g16};
+
+  auto issue = [&](int t) {
     const int key0 = start + t * TK, valid = min(TK, end - key0);
-    const auto r = make_rsrc(vbase + (size_t)key0 * rstride, (uint32_t)(valid - 1) * rstride + ROWB);
+    FA_LDS char* dst = ring + (t % GQA_NS) * STAGE;
+    const uint32_t bytes = (uint32_t)(valid - 1) * rstride + ROWB;
+    const auto rk = make_rsrc(kbase + (size_t)key0 * rstride, bytes);
+    const auto rv = make_rsrc(vbase + (size_t)key0 * rstride, bytes);
     if (valid == TK) {
 #pragma unroll
-      for (int i = 0; i < VT / 1024; i++) dma16_buf(r, dst + i * 1024, voff[i]);
+      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rk, dst + i * 1024, kcoff[i]);
+#pragma unroll
+      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rv, dst + TILE + i * 1024, vcoff[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < VT / 1024; i++) {
+      for (int i = 0; i < TILE / 1024; i++) {
         const uint32_t row = 8 * i + lane / 8, rc = min(row, (uint32_t)(valid - 1));
-        dma16_buf(r, dst + i * 1024, rc * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4));
+        dma16_buf(rk, dst + i * 1024, rc * rstride + (((lane & 7) ^ swz_half(row)) << 4));
+        dma16_buf(rv, dst + TILE + i * 1024, rc * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4));
       }
     }
     // scales of keys key0 + lane (lanes past the tile repeat its last key)
     const uint32_t so = (uint32_t)min(lane, valid - 1) * sstride;
     const uint32_t sbytes = (uint32_t)(valid - 1) * sstride + 4;
-    dma4_buf(make_rsrc(ksbase + (size_t)key0 * a.Hkv, sbytes), dst + VT, so);
-    dma4_buf(make_rsrc(vsbase + (size_t)key0 * a.Hkv, sbytes), dst + VT + SCB, so);
+    dma4_buf(make_rsrc(ksbase + (size_t)key0 * a.Hkv, sbytes), dst + 2 * TILE, so);
+    dma4_buf(make_rsrc(vsbase + (size_t)key0 * a.Hkv, sbytes), dst + 2 * TILE + SCB, so);
   };
 
   float m_ref = -INFINITY, neg = 0.f, l = 0.f;
@@ -301,33 +339,44 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
 #pragma unroll
   for (int d = 0; d < D / 16; d++) o[d] = f32x4_t{};
 
-  // tile t: K(t) in kf[t & 1] (issued two tiles earlier), V(t) and its scales in
-  // vst[t & 1] (one tile earlier).  Issue order per tile: V(t+1), then K(t+2).
-  auto tile = [&](auto SLOT, int t) {
-    constexpr int sl = decltype(SLOT)::value;
-    if (t + 1 < n_tiles) issue_v(t + 1, vst[sl ^ 1]);
+  // same ring discipline as the bf16 kernel: GQA_NS - 1 tiles of copies in flight
+#pragma unroll
+  for (int p = 0; p < GQA_NS - 1; p++) issue(min(p, n_tiles - 1));
+  for (int t = 0; t < n_tiles; t++) {
+    issue(min(t + GQA_NS - 1, n_tiles - 1));
+    wait_vmcnt<(GQA_NS - 1) * OPS>();
+    asm volatile("" ::: "memory");
+    const uint32_t st = lds_addr(ring) + (t % GQA_NS) * STAGE;
+
+    i32x4_t kf[4], sc[4];
+    {
+      uint32_t ad[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        ad[i] = st + ka[i];
+        ad[4 + i] = st + sa[i];
+      }
+      i32x4_t r[8];
+      lds_b128_x8(r, ad);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        kf[i] = r[i];
+        sc[i] = r[4 + i];
+      }
+    }
     f32x4_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
       s[kb] = f32x4_t{};
 #pragma unroll
       for (int hh = 0; hh < 2; hh++) {
-        const i32x4_t w = kf[sl][kb][hh];
+        const i32x4_t w = kf[2 * kb + hh];
         s[kb] = mfma16x16x32_bf16(e4m3x8_to_bf16(i32x2_t{w.x, w.y}), qf[2 * hh], s[kb]);
         s[kb] = mfma16x16x32_bf16(e4m3x8_to_bf16(i32x2_t{w.z, w.w}), qf[2 * hh + 1], s[kb]);
       }
     }
-    if (t + 2 < n_tiles) issue_k(t + 2, kf[sl]);
-    // V(t) and the scales of tile t must have landed: later vector-memory ops are K(t+1),
-    // V(t+1) with its scales, K(t+2)
-    if (t + 2 < n_tiles) wait_vmcnt<2 * KOPS + VOPS>();
-    else if (t + 1 < n_tiles) wait_vmcnt<KOPS + VOPS>();
-    else wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    const FA_LDS char* vt = vst[sl];
-    // register v of block kb holds key 16kb + 4g + v
-    const f32x4_t ks0 = lds_f32x4(vt + VT + 16 * g), ks1 = lds_f32x4(vt + VT + 64 + 16 * g);
-    const f32x4_t vs0 = lds_f32x4(vt + VT + SCB + 16 * g), vs1 = lds_f32x4(vt + VT + SCB + 64 + 16 * g);
+    const f32x4_t ks0 = __builtin_bit_cast(f32x4_t, sc[0]), ks1 = __builtin_bit_cast(f32x4_t, sc[1]);
+    const f32x4_t vs0 = __builtin_bit_cast(f32x4_t, sc[2]), vs1 = __builtin_bit_cast(f32x4_t, sc[3]);
 #pragma unroll
     for (int v = 0; v < 4; v++) {
       s[0][v] *= ks0[v];
@@ -364,19 +413,17 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
       }
     const i32x4_t pb = {pack_bf16(e[0] * vs0[0], e[1] * vs0[1]), pack_bf16(e[2] * vs0[2], e[3] * vs0[3]),
                         pack_bf16(e[4] * vs1[0], e[5] * vs1[1]), pack_bf16(e[6] * vs1[2], e[7] * vs1[3])};
+    i32x2_t vr[D / 16];
+    {
+      uint32_t ad[D / 16];
 #pragma unroll
-    for (int db = 0; db < D / 16; db++)
-      o[db] = mfma16x16x32_bf16(e4m3x8_to_bf16(lds_tr8(vt + vrd + ((db ^ vsw) << 4))), pb, o[db]);
-  };
-
-  issue_k(0, kf[0]);
-  issue_v(0, vst[0]);
-  if (1 < n_tiles) issue_k(1, kf[1]);
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 >= n_tiles) break;
-    tile(std::integral_constant<int, 1>{}, t + 1);
+      for (int db = 0; db < D / 16; db++) ad[db] = st + va[db];
+      lds_tr8_x8(vr, ad);
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; db++) o[db] = mfma16x16x32_bf16(e4m3x8_to_bf16(vr[db]), pb, o[db]);
   }
+  wait_vmcnt<0>();  // the repeat copies past the end land before the LDS is released
 
   const float l_tot = xor32_sum(xor16_sum(l));
   if (l16 < G) {
@@ -868,7 +915,7 @@ size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split) {
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
-  dim3 grid(a.Hkv, a.n_split, a.B);
+  const int grid = a.n_split * ((a.B + 7) / 8 * 8) * a.Hkv;  // see gqa_item
   switch (G) {
 #define FA_G(n)                                                   \
   case n:                                                         \
