@@ -76,36 +76,11 @@ __device__ __forceinline__ i32x2_t lds_tr16(const FA_LDS char* p) {
 __device__ __forceinline__ i32x2_t lds_tr8(const FA_LDS char* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2_t*)p);
 }
-// Sixteen ds_read_b64_tr_b16 at LDS byte addresses a[i], issued back to back and waited for
+// Eight ds_read_b64_tr_b16 at LDS byte addresses a[i], issued back to back and waited for
 // once, in one asm statement: the reads overlap, and the compiler, which sees no LDS read here,
 // adds no wait of its own for direct-to-LDS copies still in flight into other buffers -- the
 // caller must already have waited (s_waitcnt vmcnt) for the copies of the data read here.
 // Outputs are early-clobber: a read may land before a later read of the block issues.
-__device__ __forceinline__ void lds_tr16_x16(i32x2_t (&r)[16], const uint32_t (&a)[16]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %17\n\t"
-      "ds_read_b64_tr_b16 %2, %18\n\t"
-      "ds_read_b64_tr_b16 %3, %19\n\t"
-      "ds_read_b64_tr_b16 %4, %20\n\t"
-      "ds_read_b64_tr_b16 %5, %21\n\t"
-      "ds_read_b64_tr_b16 %6, %22\n\t"
-      "ds_read_b64_tr_b16 %7, %23\n\t"
-      "ds_read_b64_tr_b16 %8, %24\n\t"
-      "ds_read_b64_tr_b16 %9, %25\n\t"
-      "ds_read_b64_tr_b16 %10, %26\n\t"
-      "ds_read_b64_tr_b16 %11, %27\n\t"
-      "ds_read_b64_tr_b16 %12, %28\n\t"
-      "ds_read_b64_tr_b16 %13, %29\n\t"
-      "ds_read_b64_tr_b16 %14, %30\n\t"
-      "ds_read_b64_tr_b16 %15, %31\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
-      : "memory");
-}
-
-// Eight ds_read_b64_tr_b16, issued and waited for as one block (see lds_tr16_x16).
 __device__ __forceinline__ void lds_tr16_x8(i32x2_t (&r)[8], const uint32_t (&a)[8]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8\n\t"
@@ -121,7 +96,7 @@ __device__ __forceinline__ void lds_tr16_x8(i32x2_t (&r)[8], const uint32_t (&a)
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
-// Eight ds_read_b64_tr_b8, issued and waited for as one block (see lds_tr16_x16).
+// Eight ds_read_b64_tr_b8, issued and waited for as one block (see lds_tr16_x8).
 __device__ __forceinline__ void lds_tr8_x8(i32x2_t (&r)[8], const uint32_t (&a)[8]) {
   asm volatile(
       "ds_read_b64_tr_b8 %0, %8\n\t"
@@ -137,8 +112,7 @@ __device__ __forceinline__ void lds_tr8_x8(i32x2_t (&r)[8], const uint32_t (&a)[
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
-
-// Eight 16-byte LDS reads, issued and waited for as one block (see lds_tr16_x16).
+// Eight 16-byte LDS reads, issued and waited for as one block (see lds_tr16_x8).
 __device__ __forceinline__ void lds_b128_x8(i32x4_t (&r)[8], const uint32_t (&a)[8]) {
   asm volatile(
       "ds_read_b128 %0, %8\n\t"
@@ -152,18 +126,6 @@ __device__ __forceinline__ void lds_b128_x8(i32x4_t (&r)[8], const uint32_t (&a)
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
-      : "memory");
-}
-// Four 16-byte LDS reads, issued and waited for as one block (see lds_tr16_x16).
-__device__ __forceinline__ void lds_b128_x4(i32x4_t (&r)[4], const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
       : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const FA_LDS char* p) { return (uint32_t)(uintptr_t)p; }
