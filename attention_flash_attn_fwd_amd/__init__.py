@@ -28,7 +28,7 @@ EXPORTS = {
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "attn_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
-    "mla_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 9 + [ctypes.c_int] * 10 +
+    "mla_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int] * 11 +
                         [ctypes.c_float, ctypes.c_void_p]),
     "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "mla_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 +
@@ -189,14 +189,22 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=N
 
 
 def mla_prefill(q_nope, q_rope, k_nope, k_rope, v, q_scale=None, k_scale=None, causal: bool = True,
-                scale: float | None = None, out=None, return_lse: bool = False):
+                scale: float | None = None, out=None, return_lse: bool = False, v_scale=None):
     """MLA prefill.  q_nope/k_nope [B,S,H,128] e4m3 (uint8 codes or float8_e4m3fn) or bf16;
-    q_rope [B,Sq,H,64], k_rope [B,Skv,Hr,64], v [B,Skv,H,128] bf16; q_scale [B,Sq,H], k_scale [B,Skv,H] fp32."""
+    q_rope [B,Sq,H,64], k_rope [B,Skv,Hr,64]; q_scale [B,Sq,H], k_scale [B,Skv,H] fp32;
+    v [B,Skv,H,128] bf16, or e4m3 codes with v_scale [B,Skv,H] fp32 (V = code * v_scale)."""
     fp8 = q_nope.dtype in _FP8
     ndt = _FP8 if fp8 else (torch.bfloat16,)
     _need(q_nope, "q_nope", ndt, 4); _need(k_nope, "k_nope", ndt, 4)
     _need(q_rope, "q_rope", (torch.bfloat16,), 4); _need(k_rope, "k_rope", (torch.bfloat16,), 4)
-    _need(v, "v", (torch.bfloat16,), 4)
+    v_fp8 = v.dtype in _FP8
+    _need(v, "v", _FP8 if v_fp8 else (torch.bfloat16,), 4)
+    if v_fp8:
+        _need(v_scale, "v_scale", (torch.float32,), 3)
+        if tuple(v_scale.shape) != tuple(v.shape[:3]):
+            raise ValueError("v_scale must be [B, Skv, H]")
+    elif v_scale is not None:
+        raise ValueError("v_scale goes with e4m3 V only")
     B, Sq, H, Dn = q_nope.shape
     Skv, Dr, Hr, Dv = k_nope.shape[1], q_rope.shape[3], k_rope.shape[2], v.shape[3]
     for t, n in ((q_scale, "q_scale"), (k_scale, "k_scale")):
@@ -213,7 +221,8 @@ def mla_prefill(q_nope, q_rope, k_nope, k_rope, v, q_scale=None, k_scale=None, c
     o = torch.empty((B, Sq, H, Dv), dtype=torch.bfloat16, device=v.device) if out is None else out
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=v.device) if return_lse else None
     st = lib().mla_prefill_fwd(_ptr(q_nope), _ptr(q_rope), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(o),
-                               _ptr(q_scale), _ptr(k_scale), _ptr(lse), ATTN_FP8_E4M3 if fp8 else ATTN_BF16,
+                               _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(lse),
+                               ATTN_FP8_E4M3 if fp8 else ATTN_BF16, ATTN_FP8_E4M3 if v_fp8 else ATTN_BF16,
                                B, Sq, Skv, H, Hr, Dn, Dr, Dv, int(bool(causal)), scale, _stream())
     _check("mla_prefill_fwd", st)
     return (o, lse) if return_lse else o

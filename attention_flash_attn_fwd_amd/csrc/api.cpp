@@ -140,10 +140,13 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
 }
 
 int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope, const void* k_rope, const void* v,
-                    void* o, const float* q_scale, const float* k_scale, float* lse, int nope_dtype, int B, int Sq,
-                    int Skv, int H, int Hr, int Dn, int Dr, int Dv, int causal, float softmax_scale,
-                    hipStream_t stream) {
+                    void* o, const float* q_scale, const float* k_scale, const float* v_scale, float* lse,
+                    int nope_dtype, int v_dtype, int B, int Sq, int Skv, int H, int Hr, int Dn, int Dr, int Dv,
+                    int causal, float softmax_scale, hipStream_t stream) {
   if (nope_dtype != ATTN_FP8_E4M3 && nope_dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  if (v_dtype != ATTN_FP8_E4M3 && v_dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+  const bool v_fp8 = v_dtype == ATTN_FP8_E4M3;
+  if (!v_fp8 && v_scale) return ATTN_ERR_DTYPE;  // the value scale belongs to e4m3 V only
   if (B < 0 || Sq < 0 || Skv < 0 || H <= 0 || Hr <= 0 || Dn <= 0 || Dr <= 0 || Dv <= 0) return ATTN_ERR_SHAPE;
   if (Hr != 1 && Hr != H) return ATTN_ERR_SHAPE;
   if (elems({B, Sq, H, Dn + Dr + Dv}) < 0 || elems({B, Skv, H, Dn + Dr + Dv}) < 0) return ATTN_ERR_SHAPE;
@@ -152,13 +155,14 @@ int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope, 
   if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
   if (B == 0 || Sq == 0) return ATTN_OK;
   if (!q_nope || !q_rope || !o || (Skv > 0 && (!k_nope || !k_rope || !v))) return ATTN_ERR_NULL;
+  if (v_fp8 && Skv > 0 && !v_scale) return ATTN_ERR_NULL;
   fa::PrefillArgs a{};
   a.q = q_nope; a.k = k_nope; a.v = v; a.o = o; a.lse = lse;
-  a.q_rope = q_rope; a.k_rope = k_rope; a.q_scale = q_scale; a.k_scale = k_scale;
+  a.q_rope = q_rope; a.k_rope = k_rope; a.q_scale = q_scale; a.k_scale = k_scale; a.v_scale = v_scale;
   a.B = B; a.Sq = Sq; a.Skv = Skv; a.Hq = H; a.Hkv = H; a.Hr = Hr;
   a.causal = causal ? 1 : 0;
   a.scale = softmax_scale;
-  return hip_status(fa::launch_mla_prefill(a, nope_dtype == ATTN_FP8_E4M3, stream));
+  return hip_status(fa::launch_mla_prefill(a, nope_dtype == ATTN_FP8_E4M3, v_fp8, stream));
 }
 
 size_t mla_decode_workspace_size(int B, int H, int Dv, int max_kv_len) {

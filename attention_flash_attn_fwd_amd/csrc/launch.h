@@ -17,6 +17,7 @@ struct PrefillArgs {
   const void* k_rope;   // MLA only
   const float* q_scale; // MLA only, nullable (= 1)
   const float* k_scale; // MLA only, nullable (= 1)
+  const float* v_scale; // MLA with e4m3 V only: one fp32 scale per V row
   const int32_t* cu_q;  // ragged batches only: query / key row offsets [B+1] of each sequence
   const int32_t* cu_k;
   int total_q, total_k; // ragged batches: rows of the packed q and k/v tensors
@@ -63,7 +64,7 @@ struct QuantArgs {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, int D, hipStream_t s);
-hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, hipStream_t s);
+hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, bool v_fp8, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, bool bf16, hipStream_t s);
 int quantize_lanes_per_row(int cols);
 hipError_t launch_quantize_rows(const QuantArgs& a, hipStream_t s);

@@ -40,7 +40,23 @@ __device__ __forceinline__ uint32_t swz_rows(uint32_t row) {
 // loads.  LDS row r holds tile row r with its chunks XOR-permuted by swz_rows(r): each lane
 // fetches the global chunk that belongs at its LDS slot.  Per-lane source offsets are
 // computed once; a tile costs one instruction per wave per KiB.
+// 16-byte chunk swizzle of an e4m3 V tile (128-byte rows): the transposing byte reads of a
+// half-wave cover the rows {r, r+1, r+2, r+3, r+8, .., r+11} (r = 0 or 4, the key order of
+// P^T) at two adjacent chunks; rows alternate bank halves by parity, and XOR-ing the chunk
+// with 2 * (bit 1 of the row | bit 3 of the row << 1) puts the 4 rows of each parity at the
+// two chunks on 8 distinct 16-byte slots of their half, so the half-wave reads all 64 banks
+// once.
+__device__ __forceinline__ uint32_t swz_v8(uint32_t row) { return (((row >> 1) & 1u) | ((row >> 2) & 2u)) << 1; }
+
 template <int ROWB>
+struct DefaultSwz {
+  __device__ __forceinline__ static uint32_t f(uint32_t row) { return swz_rows<ROWB>(row); }
+};
+struct SwzV8 {
+  __device__ __forceinline__ static uint32_t f(uint32_t row) { return swz_v8(row); }
+};
+
+template <int ROWB, class SWZ = DefaultSwz<ROWB>>
 struct RowDma {
   static constexpr int RPI = 1024 / ROWB;           // rows per wave instruction
   static constexpr int CPR = ROWB / 16;             // 16-byte chunks per row
@@ -52,7 +68,7 @@ struct RowDma {
 #pragma unroll
     for (int i = 0; i < NI; i++) {
       const uint32_t row = (i * NW + wave) * RPI + lane / CPR;
-      voff[i] = row * stride + ((((uint32_t)lane % CPR) ^ swz_rows<ROWB>(row)) << 4);
+      voff[i] = row * stride + ((((uint32_t)lane % CPR) ^ SWZ::f(row)) << 4);
     }
   }
   // Rows [0, valid) of the tile start at `base`, `stride` bytes apart; LDS rows at or past
@@ -68,7 +84,7 @@ struct RowDma {
       for (int i = 0; i < NI; i++) {
         const uint32_t row = (i * NW + wave) * RPI + lane / CPR;
         const uint32_t rc = min(row, (uint32_t)(valid - 1));
-        dma16_buf(r, dst + (i * NW + wave) * 1024, rc * stride + ((((uint32_t)lane % CPR) ^ swz_rows<ROWB>(row)) << 4));
+        dma16_buf(r, dst + (i * NW + wave) * 1024, rc * stride + ((((uint32_t)lane % CPR) ^ SWZ::f(row)) << 4));
       }
     }
   }
@@ -242,11 +258,113 @@ __device__ __forceinline__ void tile_scores(f32x16_t (&s)[BN / 32], const typena
   for (int kb = 0; kb < BN / 32; kb++) QK::scores(q, ks, kst, kb, hl, s[kb], has_ks);
 }
 
-// Mask, row max, lazy rescale of O and l, then P^T = exp2(S^T c - m c) packed to bf16 and
-// the row sums of the packed values.
-template <int DV, bool CAUSAL>
-__device__ __forceinline__ void tile_softmax(RowAcc<DV>& st, f32x16_t (&s)[BN / 32], i32x4_t (&pb)[BN / 32][2],
-                                             int key0, bool masked, int qrow, int off, int Skv, float c, int hl) {
+// ------------------------------------------------------------------------------------
+// V policies: the V part of an LDS stage, its copy, the per-key factor folded into P, and
+// O^T += V^T . P^T over one tile.
+
+// bf16 V (rows of DV bf16), read transposed two bytes wide.
+template <int DV_>
+struct VBf16 {
+  static constexpr int DV = DV_;
+  static constexpr int ROWB = DV * 2;
+  static constexpr int BYTES = BN * ROWB;
+  static constexpr bool SCALED = false;
+  struct Lane {
+    RowDma<ROWB> dma;
+    uint32_t va[2][DV / 32];
+  };
+  __device__ static void init(const PrefillArgs& p, int wave, int lane, Lane& s) {
+    s.dma.init(wave, lane, p.Hkv * ROWB);
+    const uint32_t g = lane >> 4, i16 = lane & 15;
+    const uint32_t row0 = 4 * (g >> 1) + (i16 >> 2), col0 = 16 * (g & 1) + 4 * (i16 & 3);
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int db = 0; db < DV / 32; db++) {
+        const uint32_t row = row0 + 8 * u, col = col0 + 32 * db;
+        s.va[u][db] = row * ROWB + ((((col >> 3)) ^ swz_rows<ROWB>(row)) << 4) + (((col >> 2) & 1) << 3);
+      }
+  }
+  __device__ static void issue(const PrefillArgs& p, const Lane& s, int b, int h, int kvh, int key0, FA_LDS char* dst,
+                               int wave, int lane) {
+    (void)h;
+    s.dma.issue((const char*)p.v + (((size_t)b * p.Skv + key0) * p.Hkv + kvh) * (size_t)ROWB, p.Hkv * ROWB,
+                min(BN, p.Skv - key0), dst, wave, lane);
+  }
+  __device__ static f32x4_t scale4(const FA_LDS char*, int, int) { return f32x4_t{1.f, 1.f, 1.f, 1.f}; }
+  // P^T block (kb, tp) -> O^T
+  __device__ static void pv(RowAcc<DV>& st, const i32x4_t& pb, const Lane& s, const FA_LDS char* vst, int kb, int tp) {
+#pragma unroll
+    for (int db = 0; db < DV / 32; db++) {
+      const int rows = (32 * kb + 16 * tp) * ROWB;
+      const i32x2_t lo = lds_tr16(vst + s.va[0][db] + rows);
+      const i32x2_t hi = lds_tr16(vst + s.va[1][db] + rows);
+      st.o[db] = mfma32x32x16_bf16(cat(lo, hi), pb, st.o[db]);
+    }
+  }
+};
+
+// e4m3 V (rows of DV codes) with one fp32 scale per key row: V = code * v_scale.  The codes
+// are read transposed one byte wide (ds_read_b64_tr_b8: 8 keys of one column per lane, one
+// read per product) and converted to bf16 exactly; the scale is folded into P, so
+// O^T += V_code^T . (P . v_scale)^T runs on the bf16 matrix cores.
+// V part of a stage: codes [BN][DV] | v_scale [BN] fp32.
+template <int DV_>
+struct VE4m3 {
+  static constexpr int DV = DV_;
+  static constexpr int ROWB = DV;
+  static constexpr int VS = BN * ROWB;
+  static constexpr int BYTES = VS + BN * 4;
+  static constexpr bool SCALED = true;
+  struct Lane {
+    RowDma<ROWB, SwzV8> dma;
+    uint32_t va[DV / 32];
+    uint32_t sa;
+  };
+  __device__ static void init(const PrefillArgs& p, int wave, int lane, Lane& s) {
+    s.dma.init(wave, lane, p.Hkv * ROWB);
+    // 16-lane group gq: lane 2e + h reads key row 8(e/4) + 4(gq/2) + e%4 at byte
+    // 32db + 16(gq%2) + 8h, so lane L receives column 32db + L%32 of the keys
+    // 8(e/4) + 4(L/32) + e%4, e = 0..7 -- the key order of P^T (the S^T accumulator layout)
+    const uint32_t gq = lane >> 4, i = lane & 15, e = i >> 1, hb = i & 1;
+    const uint32_t row0 = 8 * (e >> 2) + 4 * (gq >> 1) + (e & 3);
+#pragma unroll
+    for (int db = 0; db < DV / 32; db++)
+      s.va[db] = row0 * ROWB + (((2 * db + (gq & 1)) ^ swz_v8(row0)) << 4) + 8 * hb;
+    s.sa = VS + 16 * (lane >> 5);
+  }
+  __device__ static void issue(const PrefillArgs& p, const Lane& s, int b, int h, int kvh, int key0, FA_LDS char* dst,
+                               int wave, int lane) {
+    (void)h;
+    const int valid = min(BN, p.Skv - key0);
+    const size_t row = ((size_t)b * p.Skv + key0) * p.Hkv + kvh;
+    s.dma.issue((const char*)p.v + row * ROWB, p.Hkv * ROWB, valid, dst, wave, lane);
+    if (wave == 0) {
+      const auto r = make_rsrc(p.v_scale + row, (uint32_t)((valid - 1) * p.Hkv + 1) * 4);
+      dma4_buf(r, dst + VS, (uint32_t)min(lane, valid - 1) * p.Hkv * 4);
+    }
+  }
+  // v_scale of keys 32kb + 16tp + 8j + 4hl .. +3 (the keys of P^T register 4j .. 4j+3)
+  __device__ static f32x4_t scale4(const FA_LDS char* vst, int kb, int tp_j) {
+    (void)kb;
+    return lds_f32x4(vst + tp_j);
+  }
+  __device__ static void pv(RowAcc<DV>& st, const i32x4_t& pb, const Lane& s, const FA_LDS char* vst, int kb, int tp) {
+#pragma unroll
+    for (int db = 0; db < DV / 32; db++) {
+      const i32x2_t w = lds_tr8(vst + s.va[db] + (32 * kb + 16 * tp) * ROWB);
+      st.o[db] = mfma32x32x16_bf16(e4m3x8_to_bf16(w), pb, st.o[db]);
+    }
+  }
+};
+
+// Mask, row max, lazy rescale of O and l, then P^T = exp2(S^T c - m c) (times the V
+// policy's per-key factor) packed to bf16, and the row sums of P.
+template <class VP, bool CAUSAL>
+__device__ __forceinline__ void tile_softmax(RowAcc<VP::DV>& st, f32x16_t (&s)[BN / 32], i32x4_t (&pb)[BN / 32][2],
+                                             const typename VP::Lane& vl, const FA_LDS char* vst, int key0,
+                                             bool masked, int qrow, int off, int Skv, float c, int hl) {
+  constexpr int DV = VP::DV;
   if (masked) {
     // register v of block kb holds key key0 + 4hl + (32kb + 8(v/4) + v%4): visible iff
     // that constant offset is below lim
@@ -279,39 +397,34 @@ __device__ __forceinline__ void tile_softmax(RowAcc<DV>& st, f32x16_t (&s)[BN / 
       float e[8];
 #pragma unroll
       for (int i = 0; i < 8; i++) e[i] = exp2_fast(fmaf(s[kb][8 * tp + i], c, st.neg));
-      pb[kb][tp] = i32x4_t{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
+      if constexpr (VP::SCALED) {
+        // register 8tp + i holds key 32kb + 16tp + 8(i/4) + 4hl + i%4
+        const f32x4_t f0 = VP::scale4(vst, kb, vl.sa + (32 * kb + 16 * tp) * 4);
+        const f32x4_t f1 = VP::scale4(vst, kb, vl.sa + (32 * kb + 16 * tp + 8) * 4);
 #pragma unroll
-      for (int i = 0; i < 4; i++) st.l = dot2_bf16(pb[kb][tp][i], kBf16PairOne, st.l);
+        for (int i = 0; i < 8; i++) st.l += e[i];
+        pb[kb][tp] = i32x4_t{pack_bf16(e[0] * f0[0], e[1] * f0[1]), pack_bf16(e[2] * f0[2], e[3] * f0[3]),
+                             pack_bf16(e[4] * f1[0], e[5] * f1[1]), pack_bf16(e[6] * f1[2], e[7] * f1[3])};
+      } else {
+        pb[kb][tp] = i32x4_t{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
+#pragma unroll
+        for (int i = 0; i < 4; i++) st.l = dot2_bf16(pb[kb][tp][i], kBf16PairOne, st.l);
+      }
     }
 }
 
-// O^T += V^T . P^T over one V tile (rows of DV bf16 at vst).
-template <int DV>
-__device__ __forceinline__ void tile_pv(RowAcc<DV>& st, const i32x4_t (&pb)[BN / 32][2],
-                                        const uint32_t (&va)[2][DV / 32], const FA_LDS char* vst) {
-  constexpr int VROWB = DV * 2;
-#pragma unroll
-  for (int kb = 0; kb < BN / 32; kb++)
-#pragma unroll
-    for (int tp = 0; tp < 2; tp++)
-#pragma unroll
-      for (int db = 0; db < DV / 32; db++) {
-        const int rows = (32 * kb + 16 * tp) * VROWB;
-        const i32x2_t lo = lds_tr16(vst + va[0][db] + rows);
-        const i32x2_t hi = lds_tr16(vst + va[1][db] + rows);
-        st.o[db] = mfma32x32x16_bf16(cat(lo, hi), pb[kb][tp], st.o[db]);
-      }
-}
-
-template <class QK, int DV, bool CAUSAL, int KPART>
-__device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFrag& q, const typename QK::Lane& ks,
-                                          const uint32_t (&va)[2][DV / 32], const FA_LDS char* stage, int key0,
+template <class QK, class VP, bool CAUSAL, int KPART>
+__device__ __forceinline__ void tile_step(RowAcc<VP::DV>& st, const typename QK::QFrag& q, const typename QK::Lane& ks,
+                                          const typename VP::Lane& vl, const FA_LDS char* stage, int key0,
                                           bool masked, int qrow, int off, int Skv, float c, int hl, bool has_ks) {
   f32x16_t s[BN / 32];
   tile_scores<QK>(s, q, ks, stage, hl, has_ks);
   i32x4_t pb[BN / 32][2];
-  tile_softmax<DV, CAUSAL>(st, s, pb, key0, masked, qrow, off, Skv, c, hl);
-  tile_pv<DV>(st, pb, va, stage + KPART);
+  tile_softmax<VP, CAUSAL>(st, s, pb, vl, stage + KPART, key0, masked, qrow, off, Skv, c, hl);
+#pragma unroll
+  for (int kb = 0; kb < BN / 32; kb++)
+#pragma unroll
+    for (int tp = 0; tp < 2; tp++) VP::pv(st, pb[kb][tp], vl, stage + KPART, kb, tp);
 }
 
 // ------------------------------------------------------------------------------------
@@ -319,11 +432,12 @@ __device__ __forceinline__ void tile_step(RowAcc<DV>& st, const typename QK::QFr
 // VARLEN: a ragged batch of packed sequences; sequence b owns query rows cu_q[b] ..
 // cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1.  The grid covers the longest sequence
 // (n_qblocks query blocks); a work item past its own sequence's blocks exits at once.
-template <class QK, int DV, bool CAUSAL, bool VARLEN = false>
+template <class QK, class VP, bool CAUSAL, bool VARLEN = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa, int n_qblocks) {
+  constexpr int DV = VP::DV;
   constexpr int KPART = (QK::KBYTES + 1023) / 1024 * 1024;
-  constexpr int VROWB = DV * 2;
-  constexpr int STAGE = KPART + BN * VROWB;
+  constexpr int OROWB = DV * 2;  // bf16 output row
+  constexpr int STAGE = KPART + VP::BYTES;
   // One LDS object per stage: the compiler then sees that reads of one stage cannot alias
   // the direct copies into the other and does not wait for those copies before reading.
   __shared__ __attribute__((aligned(1024))) char stage0_raw[STAGE];
@@ -368,9 +482,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa, int n_q
     n_qblocks = (p.Sq + BM - 1) / BM;
     if (it >= (CAUSAL ? (n_qblocks + 1) / 2 : n_qblocks)) return;
     p.q = (const char*)p.q + (size_t)q0 * p.Hq * QK::ROWB;
-    p.o = (char*)p.o + (size_t)q0 * p.Hq * (DV * 2);
+    p.o = (char*)p.o + (size_t)q0 * p.Hq * OROWB;
     p.k = (const char*)p.k + (size_t)k0 * p.Hkv * QK::ROWB;
-    p.v = (const char*)p.v + (size_t)k0 * p.Hkv * (DV * 2);
+    p.v = (const char*)p.v + (size_t)k0 * p.Hkv * VP::ROWB;
     lse_off = (size_t)q0;
     lse_hs = (size_t)p.total_q;
     b = 0;  // the pointers now start at the sequence
@@ -385,20 +499,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa, int n_q
 
   typename QK::Lane kl;
   QK::init(p, wave, lane, kl);
-  RowDma<VROWB> vdma;
-  vdma.init(wave, lane, p.Hkv * VROWB);
-  uint32_t va[2][DV / 32];
-  {
-    const uint32_t g = lane >> 4, i16 = lane & 15;
-    const uint32_t row0 = 4 * (g >> 1) + (i16 >> 2), col0 = 16 * (g & 1) + 4 * (i16 & 3);
-#pragma unroll
-    for (int u = 0; u < 2; u++)
-#pragma unroll
-      for (int db = 0; db < DV / 32; db++) {
-        const uint32_t row = row0 + 8 * u, col = col0 + 32 * db;
-        va[u][db] = row * VROWB + ((((col >> 3)) ^ swz_rows<VROWB>(row)) << 4) + (((col >> 2) & 1) << 3);
-      }
-  }
+  typename VP::Lane vl;
+  VP::init(p, wave, lane, vl);
   const float c = p.scale * kLog2e;
   const int off = p.Skv - p.Sq;
   const bool has_ks = p.k_scale != nullptr;
@@ -406,8 +508,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa, int n_q
   auto issue = [&](int t, FA_LDS char* dst) {
     const int key0 = t * BN;
     QK::issue(p, kl, b, h, kvh, key0, dst, wave, lane);
-    vdma.issue((const char*)p.v + (((size_t)b * p.Skv + key0) * p.Hkv + kvh) * (size_t)VROWB, p.Hkv * VROWB,
-               min(BN, p.Skv - key0), dst + KPART, wave, lane);
+    VP::issue(p, vl, b, h, kvh, key0, dst + KPART, wave, lane);
   };
 
   for (int bi = 0; bi < nblk; bi++) {
@@ -441,13 +542,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa, int n_q
       barrier();
       if (t + 1 < n_tiles) issue(t + 1, stage1);
       if (t < wave_tiles)
-        tile_step<QK, DV, CAUSAL, KPART>(st, qf, kl, va, stage0, t * BN, t >= mask_from, qrow, off, p.Skv, c, hl, has_ks);
+        tile_step<QK, VP, CAUSAL, KPART>(st, qf, kl, vl, stage0, t * BN, t >= mask_from, qrow, off, p.Skv, c, hl, has_ks);
       if (t + 1 >= n_tiles) break;
       wait_vmcnt<0>();
       barrier();
       if (t + 2 < n_tiles) issue(t + 2, stage0);
       if (t + 1 < wave_tiles)
-        tile_step<QK, DV, CAUSAL, KPART>(st, qf, kl, va, stage1, (t + 1) * BN, t + 1 >= mask_from, qrow, off, p.Skv, c,
+        tile_step<QK, VP, CAUSAL, KPART>(st, qf, kl, vl, stage1, (t + 1) * BN, t + 1 >= mask_from, qrow, off, p.Skv, c,
                                          hl, has_ks);
     }
 
@@ -455,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pa, int n_q
     const float l_tot = xor32_sum(st.l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < p.Sq) {
-      char* ob = (char*)p.o + (((size_t)b * p.Sq + qrow) * p.Hq + h) * (size_t)VROWB;
+      char* ob = (char*)p.o + (((size_t)b * p.Sq + qrow) * p.Hq + h) * (size_t)OROWB;
 #pragma unroll
       for (int db = 0; db < DV / 32; db++)
 #pragma unroll
@@ -485,11 +586,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s) {
   const int grid = items(a, nqb);
   if (grid == 0) return hipSuccess;
   if (D == 128) {
-    if (a.causal) prefill_kernel<QkBf16<128>, 128, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_kernel<QkBf16<128>, 128, false><<<grid, 256, 0, s>>>(a, nqb);
+    if (a.causal) prefill_kernel<QkBf16<128>, VBf16<128>, true><<<grid, 256, 0, s>>>(a, nqb);
+    else prefill_kernel<QkBf16<128>, VBf16<128>, false><<<grid, 256, 0, s>>>(a, nqb);
   } else {
-    if (a.causal) prefill_kernel<QkBf16<64>, 64, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_kernel<QkBf16<64>, 64, false><<<grid, 256, 0, s>>>(a, nqb);
+    if (a.causal) prefill_kernel<QkBf16<64>, VBf16<64>, true><<<grid, 256, 0, s>>>(a, nqb);
+    else prefill_kernel<QkBf16<64>, VBf16<64>, false><<<grid, 256, 0, s>>>(a, nqb);
   }
   return hipGetLastError();
 }
@@ -501,25 +602,31 @@ hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, int D, hipStream_t s
   const int grid = (a.B * a.Hq + 7) / 8 * 8 * per_head;
   if (grid == 0) return hipSuccess;
   if (D == 128) {
-    if (a.causal) prefill_kernel<QkBf16<128>, 128, true, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_kernel<QkBf16<128>, 128, false, true><<<grid, 256, 0, s>>>(a, nqb);
+    if (a.causal) prefill_kernel<QkBf16<128>, VBf16<128>, true, true><<<grid, 256, 0, s>>>(a, nqb);
+    else prefill_kernel<QkBf16<128>, VBf16<128>, false, true><<<grid, 256, 0, s>>>(a, nqb);
   } else {
-    if (a.causal) prefill_kernel<QkBf16<64>, 64, true, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_kernel<QkBf16<64>, 64, false, true><<<grid, 256, 0, s>>>(a, nqb);
+    if (a.causal) prefill_kernel<QkBf16<64>, VBf16<64>, true, true><<<grid, 256, 0, s>>>(a, nqb);
+    else prefill_kernel<QkBf16<64>, VBf16<64>, false, true><<<grid, 256, 0, s>>>(a, nqb);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, hipStream_t s) {
+template <class QK, class VP>
+void launch_mla(const PrefillArgs& a, int grid, int nqb, hipStream_t s) {
+  if (a.causal) prefill_kernel<QK, VP, true><<<grid, 256, 0, s>>>(a, nqb);
+  else prefill_kernel<QK, VP, false><<<grid, 256, 0, s>>>(a, nqb);
+}
+
+hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, bool v_fp8, hipStream_t s) {
   int nqb;
   const int grid = items(a, nqb);
   if (grid == 0) return hipSuccess;
   if (nope_fp8) {
-    if (a.causal) prefill_kernel<QkMla<true>, 128, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_kernel<QkMla<true>, 128, false><<<grid, 256, 0, s>>>(a, nqb);
+    if (v_fp8) launch_mla<QkMla<true>, VE4m3<128>>(a, grid, nqb, s);
+    else launch_mla<QkMla<true>, VBf16<128>>(a, grid, nqb, s);
   } else {
-    if (a.causal) prefill_kernel<QkMla<false>, 128, true><<<grid, 256, 0, s>>>(a, nqb);
-    else prefill_kernel<QkMla<false>, 128, false><<<grid, 256, 0, s>>>(a, nqb);
+    if (v_fp8) launch_mla<QkMla<false>, VE4m3<128>>(a, grid, nqb, s);
+    else launch_mla<QkMla<false>, VBf16<128>>(a, grid, nqb, s);
   }
   return hipGetLastError();
 }

@@ -72,8 +72,9 @@ def algorithmic_work(w, lens=None):
     if w.kind == "mla_prefill":
         pairs = w.Sq * (w.Sq + 1) // 2 if w.causal else w.Sq * w.Skv
         f_fp8 = 2 * w.Dn * pairs * w.B * w.Hq
-        f_bf16 = 2 * (w.Dr + w.Dv) * pairs * w.B * w.Hq
-        byts = w.B * (w.Sq * w.Hq * (w.Dn + 2 * w.Dr + 2 * w.Dv + 4) + w.Skv * w.Hq * (w.Dn + 2 * w.Dv + 4)
+        f_bf16 = 2 * (w.Dr + w.Dv) * pairs * w.B * w.Hq          # rope QK and P.V on bf16 matrix cores
+        vbytes = w.Dv + 4 if w.dtype == "fp8v" else 2 * w.Dv    # e4m3 codes + scale, or bf16
+        byts = w.B * (w.Sq * w.Hq * (w.Dn + 2 * w.Dr + 2 * w.Dv + 4) + w.Skv * w.Hq * (w.Dn + 4 + vbytes)
                       + w.Skv * w.Hr * 2 * w.Dr)
         return (f_fp8, f_bf16), byts
     if w.kind == "quantize":
@@ -161,10 +162,11 @@ def setup(w):
     if w.kind == "mla_prefill":
         d = make_mla_prefill(w)
         t = {n: (bf16(d[n]) if d[n].dtype == np.uint16 else torch.from_numpy(d[n]).cuda())
-             for n in ("q_nope", "k_nope", "q_scale", "k_scale", "q_rope", "k_rope", "v")}
+             for n in ("q_nope", "k_nope", "q_scale", "k_scale", "q_rope", "k_rope", "v", "v_scale") if n in d}
         o = torch.empty((w.B, w.Sq, w.Hq, w.Dv), dtype=torch.bfloat16, device="cuda")
         return (lambda i: fa.mla_prefill(t["q_nope"], t["q_rope"], t["k_nope"], t["k_rope"], t["v"], t["q_scale"],
-                                         t["k_scale"], causal=w.causal, scale=w.scale, out=o)), None, (t, o)
+                                         t["k_scale"], causal=w.causal, scale=w.scale, out=o,
+                                         v_scale=t.get("v_scale"))), None, (t, o)
     if w.kind == "quantize":
         from workloads import make_quantize
         x = torch.from_numpy(make_quantize(w)["x"]).cuda()
@@ -196,20 +198,23 @@ def cpu_baseline(w, lens, budget_s: float):
             if b not in cache:
                 cache = {b: (make_prefill(w, batches=[b]) if w.kind == "prefill" else make_mla_prefill(w, batches=[b]))}
             d = cache[b]
+            # the inputs of this (batch, head), decoded to fp64 outside the timed region
+            if w.kind == "prefill":
+                kvh = h // (w.Hq // w.Hkv)
+                dec = oracle.bf16_to_f64 if w.dtype == "bf16" else (lambda x: x.astype(np.float64))
+                args = (dec(d["q"][:, :, h:h + 1]), dec(d["k"][:, :, kvh:kvh + 1]), dec(d["v"][:, :, kvh:kvh + 1]))
+                fn = lambda rows: oracle.prefill_rows(*args, w.scale, w.causal, 0, 0, rows)
+            else:
+                s = lambda a: a[:, :, h:h + 1]
+                vv = (oracle.e4m3_to_f64(s(d["v"])) * s(d["v_scale"])[..., None].astype(np.float64)
+                      if "v_scale" in d else oracle.bf16_to_f64(s(d["v"])))
+                args = (oracle.e4m3_to_f64(s(d["q_nope"])), oracle.bf16_to_f64(s(d["q_rope"])),
+                        oracle.e4m3_to_f64(s(d["k_nope"])), oracle.bf16_to_f64(d["k_rope"]), vv,
+                        s(d["q_scale"]).astype(np.float64), s(d["k_scale"]).astype(np.float64))
+                fn = lambda rows: oracle.mla_prefill_rows(*args, w.scale, w.causal, 0, 0, rows)
             t0 = time.perf_counter()
             for r0 in range(0, w.Sq, 1024):
-                rows = np.arange(r0, min(w.Sq, r0 + 1024))
-                if w.kind == "prefill":
-                    kvh = h // (w.Hq // w.Hkv)
-                    dec = oracle.bf16_to_f64 if w.dtype == "bf16" else (lambda x: x.astype(np.float64))
-                    oracle.prefill_rows(dec(d["q"][:, :, h:h + 1]), dec(d["k"][:, :, kvh:kvh + 1]),
-                                        dec(d["v"][:, :, kvh:kvh + 1]), w.scale, w.causal, 0, 0, rows)
-                else:
-                    s = lambda a: a[:, :, h:h + 1]
-                    oracle.mla_prefill_rows(oracle.e4m3_to_f64(s(d["q_nope"])), oracle.bf16_to_f64(s(d["q_rope"])),
-                                            oracle.e4m3_to_f64(s(d["k_nope"])), oracle.bf16_to_f64(d["k_rope"]),
-                                            oracle.bf16_to_f64(s(d["v"])), s(d["q_scale"]).astype(np.float64),
-                                            s(d["k_scale"]).astype(np.float64), w.scale, w.causal, 0, 0, rows)
+                fn(np.arange(r0, min(w.Sq, r0 + 1024)))
             t_used += time.perf_counter() - t0
             n += 1
             if t_used >= budget_s:
@@ -425,7 +430,7 @@ def main():
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "spinup_s": args.spinup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32->e4m3" if w.kind == "quantize" else "bf16 (fp32 LSE)" if w.kind == "merge" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16",
+        "dtype": "f32->e4m3" if w.kind == "quantize" else "bf16 (fp32 LSE)" if w.kind == "merge" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16", "fp8v": "e4m3 nope and V (bf16 P.V), bf16 rope",
                                                            "fp8": "e4m3 cache, bf16 q/o"}[w.dtype],
         "data": "synthetic (seeded N(0,1), see workloads/)", "config": cfg, "roofline": roof,
         "kernel_ms": round(launch_ms, 4), "algorithmic": {"flops": flops if not isinstance(flops, tuple) else list(flops),

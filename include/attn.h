@@ -141,20 +141,24 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
 /*
  * MLA prefill with per-token scales (MLASmemStorage page: Q and KV tiles each hold a
  * nope part in the qkv dtype and a rope part in the rope dtype, plus one fp32 q_scale
- * per Q row and one k_scale per K row of the tile).  Logits:
+ * per Q row and one k_scale per K row of the tile; V is typed like Q and K_nope).  Logits:
  *   x[i,j] = scale * ( (q_nope_i . k_nope_j) * q_scale_i * k_scale_j + q_rope_i . k_rope_j )
  *   q_nope [B,Sq,H,Dn], k_nope [B,Skv,H,Dn]: `nope_dtype` (ATTN_FP8_E4M3 or ATTN_BF16);
  *   q_rope [B,Sq,H,Dr], k_rope [B,Skv,Hr,Dr] (Hr = 1: one rope head shared by all H,
- *   or Hr = H): bf16; v [B,Skv,H,Dv], o [B,Sq,H,Dv]: bf16;
+ *   or Hr = H): bf16; o [B,Sq,H,Dv]: bf16;
+ *   v [B,Skv,H,Dv] of `v_dtype`: ATTN_BF16 (v_scale must be NULL), or ATTN_FP8_E4M3 codes
+ *   with one fp32 scale per V row, v_scale [B,Skv,H] (required): V = code * v_scale.  The
+ *   products P.V run on bf16 matrix cores after an exact code conversion, with v_scale
+ *   folded into P (P stays bf16: e4m3 P would cost ~2.5% relative error on O);
  *   q_scale [B,Sq,H], k_scale [B,Skv,H]: fp32, or NULL for all-ones;
  *   lse: NULL or fp32 [B,H,Sq].
  *   Supported: (Dn, Dr, Dv) == (128, 64, 128).
  */
 int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope,
                     const void* k_rope, const void* v, void* o, const float* q_scale,
-                    const float* k_scale, float* lse, int nope_dtype, int B, int Sq, int Skv,
-                    int H, int Hr, int Dn, int Dr, int Dv, int causal, float softmax_scale,
-                    hipStream_t stream);
+                    const float* k_scale, const float* v_scale, float* lse, int nope_dtype,
+                    int v_dtype, int B, int Sq, int Skv, int H, int Hr, int Dn, int Dr, int Dv,
+                    int causal, float softmax_scale, hipStream_t stream);
 
 /*
  * MLA decode (KVPipelineGeneric page, MLA decode utilities): H query heads share one

@@ -100,10 +100,10 @@ def test_decode_validation(lib):
     assert decode(lib, dtype=2, ks=FAKE, vs=FAKE, D=64) == EUNSUP
 
 
-def mla_prefill(lib, qn=FAKE, qr=FAKE, kn=FAKE, kr=FAKE, v=FAKE, o=FAKE, dt=2, B=1, Sq=64, Skv=64, H=4, Hr=1,
-                Dn=128, Dr=64, Dv=128, causal=1, scale=0.07):
-    return lib.mla_prefill_fwd(qn, qr, kn, kr, v, o, NUL, NUL, NUL, dt, B, Sq, Skv, H, Hr, Dn, Dr, Dv, causal,
-                               scale, S)
+def mla_prefill(lib, qn=FAKE, qr=FAKE, kn=FAKE, kr=FAKE, v=FAKE, o=FAKE, vs=NUL, dt=2, vdt=1, B=1, Sq=64, Skv=64,
+                H=4, Hr=1, Dn=128, Dr=64, Dv=128, causal=1, scale=0.07):
+    return lib.mla_prefill_fwd(qn, qr, kn, kr, v, o, NUL, NUL, vs, NUL, dt, vdt, B, Sq, Skv, H, Hr, Dn, Dr, Dv,
+                               causal, scale, S)
 
 
 def test_mla_prefill_validation(lib):
@@ -117,6 +117,11 @@ def test_mla_prefill_validation(lib):
     assert mla_prefill(lib, qr=NUL) == ENULL
     assert mla_prefill(lib, kr=NUL) == ENULL
     assert mla_prefill(lib, B=0, qn=NUL, qr=NUL, kn=NUL, kr=NUL, v=NUL, o=NUL) == OK
+    # e4m3 V carries one scale per row; bf16 V takes none
+    assert mla_prefill(lib, vdt=0) == EDTYPE
+    assert mla_prefill(lib, vdt=1, vs=FAKE) == EDTYPE
+    assert mla_prefill(lib, vdt=2, vs=NUL) == ENULL
+    assert mla_prefill(lib, vdt=2, vs=FAKE, Dv=64) == EUNSUP
 
 
 def mla_decode(lib, q=FAKE, kv=FAKE, o=FAKE, lens=FAKE, ks=NUL, dtype=1, B=8, H=128, Dk=576, Dv=512, L=4096,

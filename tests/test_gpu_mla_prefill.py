@@ -1,5 +1,5 @@
-"""GPU parity of mla_prefill_fwd (e4m3 nope with per-token scales + bf16 rope) against the oracle
-run on the dequantised inputs."""
+"""GPU parity of mla_prefill_fwd (e4m3 nope with per-token scales + bf16 rope; bf16 or e4m3 V)
+against the oracle run on the dequantised inputs."""
 import numpy as np
 import pytest
 import torch
@@ -14,28 +14,42 @@ pytestmark = pytest.mark.gpu
 MLA = "mla_prefill_fp8_causal_b1_h128_s8192"
 
 
+MLA8V = "mla_prefill_fp8v_causal_b1_h128_s8192"
+
+
 def _inputs(w):
     d = make_mla_prefill(w)
-    t = {k: (dev_bf16(d[k]) if d[k].dtype == np.uint16 else dev(d[k])) for k in
-         ("q_nope", "k_nope", "q_scale", "k_scale", "q_rope", "k_rope", "v")}
+    names = ("q_nope", "k_nope", "q_scale", "k_scale", "q_rope", "k_rope", "v") + (("v_scale",) if "v_scale" in d else ())
+    t = {k: (dev_bf16(d[k]) if d[k].dtype == np.uint16 else dev(d[k])) for k in names}
     return d, t
+
+
+def _v_f64(d):
+    """V as the oracle sees it: bf16 values, or e4m3 codes times their row scales."""
+    if "v_scale" in d:
+        return oracle.e4m3_to_f64(d["v"]) * d["v_scale"][..., None].astype(np.float64)
+    return oracle.bf16_to_f64(d["v"])
 
 
 def _oracle_inputs(d):
     return dict(q_nope=oracle.e4m3_to_f64(d["q_nope"]), k_nope=oracle.e4m3_to_f64(d["k_nope"]),
                 q_rope=oracle.bf16_to_f64(d["q_rope"]), k_rope=oracle.bf16_to_f64(d["k_rope"]),
-                v=oracle.bf16_to_f64(d["v"]), q_scale=d["q_scale"].astype(np.float64),
-                k_scale=d["k_scale"].astype(np.float64))
+                v=_v_f64(d), q_scale=d["q_scale"].astype(np.float64), k_scale=d["k_scale"].astype(np.float64))
 
 
+def _call(t, w, causal):
+    return fa.mla_prefill(t["q_nope"], t["q_rope"], t["k_nope"], t["k_rope"], t["v"], t["q_scale"], t["k_scale"],
+                          causal=causal, scale=w.scale, return_lse=True, v_scale=t.get("v_scale"))
+
+
+@pytest.mark.parametrize("name", [MLA, MLA8V])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("S,H,Hr", [(200, 4, 1), (333, 2, 2), (64, 3, 1)])
-def test_mla_prefill_fp8_small(causal, S, H, Hr):
-    w = workload(MLA, Sq=S, Skv=S, Hq=H, Hkv=H, Hr=Hr, causal=causal)
-    say(f"case mla prefill fp8 S={S} H={H} Hr={Hr} causal={causal}")
+def test_mla_prefill_fp8_small(name, causal, S, H, Hr):
+    w = workload(name, Sq=S, Skv=S, Hq=H, Hkv=H, Hr=Hr, causal=causal)
+    say(f"case {name} S={S} H={H} Hr={Hr} causal={causal}")
     d, t = _inputs(w)
-    o, lse = fa.mla_prefill(t["q_nope"], t["q_rope"], t["k_nope"], t["k_rope"], t["v"], t["q_scale"], t["k_scale"],
-                            causal=causal, scale=w.scale, return_lse=True)
+    o, lse = _call(t, w, causal)
     torch.cuda.synchronize()
     x = _oracle_inputs(d)
     ro, rl = oracle.mla_prefill(x["q_nope"], x["q_rope"], x["k_nope"], x["k_rope"], x["v"], x["q_scale"],
@@ -57,13 +71,14 @@ def test_mla_prefill_bf16_nope_without_scales():
     assert_close(host_f64(o), ro, BF16_TOL, "O")
 
 
-def test_mla_prefill_full_workload_sampled():
-    """The full MLA prefill workload (B1 H128 S8192, e4m3 nope + scales); sampled rows of a few heads."""
-    w = workload(MLA)
+@pytest.mark.parametrize("name", [MLA, MLA8V])
+def test_mla_prefill_full_workload_sampled(name):
+    """The full MLA prefill workload (B1 H128 S8192, e4m3 nope + scales; bf16 or e4m3 V); sampled
+    rows of a few heads."""
+    w = workload(name)
     say(f"case {w.name} (sampled rows)")
     d, t = _inputs(w)
-    o, lse = fa.mla_prefill(t["q_nope"], t["q_rope"], t["k_nope"], t["k_rope"], t["v"], t["q_scale"], t["k_scale"],
-                            causal=True, scale=w.scale, return_lse=True)
+    o, lse = _call(t, w, True)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 8191], rng.integers(0, 8192, 10)]))
@@ -72,9 +87,24 @@ def test_mla_prefill_full_workload_sampled():
         sl = lambda a: a[:, :, h:h + 1]
         ro, rl = oracle.mla_prefill_rows(
             oracle.e4m3_to_f64(sl(d["q_nope"])), oracle.bf16_to_f64(sl(d["q_rope"])),
-            oracle.e4m3_to_f64(sl(d["k_nope"])), oracle.bf16_to_f64(d["k_rope"]), oracle.bf16_to_f64(sl(d["v"])),
+            oracle.e4m3_to_f64(sl(d["k_nope"])), oracle.bf16_to_f64(d["k_rope"]), sl(_v_f64(d)),
             sl(d["q_scale"]).astype(np.float64), sl(d["k_scale"]).astype(np.float64), w.scale, True, 0, 0, rows)
         got.append(host_f64(o[0, rows, h])); ref.append(ro)
         gl.append(lse[0, h, rows].cpu().numpy()); rlse.append(rl)
     assert_close(np.stack(got), np.stack(ref), FP8_TOL, "O sampled")
     assert_lse_close(np.stack(gl), np.stack(rlse), "LSE sampled")
+
+
+def test_mla_prefill_fp8v_matches_bf16v_on_the_dequantised_values():
+    """e4m3 V with scales against bf16 V holding the dequantised values (code * scale rounded to
+    bf16): two GPU outputs, each rounded to bf16 on its own, so they may differ by a whole bf16
+    ulp (1.6e-2 for |O| in [2, 4)); held to the e4m3 path's bar."""
+    w = workload(MLA8V, Sq=300, Skv=300, Hq=3, Hkv=3)
+    d, t = _inputs(w)
+    o8, _ = _call(t, w, True)
+    vb = torch.from_numpy((oracle.e4m3_to_f64(d["v"]) * d["v_scale"][..., None]).astype(np.float32)).cuda()
+    tb = dict(t, v=vb.to(torch.bfloat16))
+    tb.pop("v_scale")
+    ob, _ = _call(tb, w, True)
+    torch.cuda.synchronize()
+    assert_close(host_f64(o8), host_f64(ob), FP8_TOL, "e4m3 V vs bf16 V")

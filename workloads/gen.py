@@ -199,6 +199,8 @@ def make_mla_prefill(w: Workload, batches=None) -> dict:
 
     q_nope/k_nope: e4m3 codes [nb, S, H, Dn] with fp32 scales [nb, S, H] (amax/448 of the fp32
     originals); q_rope [nb, S, H, Dr], k_rope [nb, S, Hr, Dr], v [nb, S, H, Dv] as bf16 bits.
+    dtype "fp8v": v as e4m3 codes with per-(token, head) fp32 scales v_scale [nb, S, H] (the same
+    draws, quantised by the same recipe).
     """
     bs = _batches(w, batches)
     nb = len(bs)
@@ -214,9 +216,16 @@ def make_mla_prefill(w: Workload, batches=None) -> dict:
     _fill(w.seed, T_KNOPE, bs, w.Skv, (H, Dn), quantize_rows_e4m3, [kn, ks])
     _fill(w.seed, T_QROPE, bs, S, (H, Dr), lambda x: (bf16_bits(x),), [qr])
     _fill(w.seed, T_KROPE, bs, w.Skv, (Hr, Dr), lambda x: (bf16_bits(x),), [kr])
-    _fill(w.seed, T_V, bs, w.Skv, (H, Dv), lambda x: (bf16_bits(x),), [v])
-    return {"q_nope": qn, "k_nope": kn, "q_scale": qs, "k_scale": ks,
-            "q_rope": qr, "k_rope": kr, "v": v, "batches": bs}
+    out = {"q_nope": qn, "k_nope": kn, "q_scale": qs, "k_scale": ks, "q_rope": qr, "k_rope": kr, "batches": bs}
+    if w.dtype == "fp8v":
+        vc = np.zeros((nb, w.Skv, H, Dv), np.uint8)
+        vs = np.zeros((nb, w.Skv, H), np.float32)
+        _fill(w.seed, T_V, bs, w.Skv, (H, Dv), quantize_rows_e4m3, [vc, vs])
+        out.update(v=vc, v_scale=vs)
+    else:
+        _fill(w.seed, T_V, bs, w.Skv, (H, Dv), lambda x: (bf16_bits(x),), [v])
+        out.update(v=v)
+    return out
 
 
 def make_quantize(w: Workload, batches=None, tokens=None) -> dict:

@@ -14,7 +14,7 @@ class Workload:
     name: str
     kind: str                 # "prefill" | "prefill_varlen" | "merge" | "decode" | "mla_prefill" | "mla_decode" | "quantize"
     seed: int
-    dtype: str                # storage dtype of q/k/v: "f32" | "bf16" | "fp8+bf16" | "fp8" (decode cache)
+    dtype: str                # storage dtype of q/k/v: "f32" | "bf16" | "fp8+bf16" | "fp8v" (MLA nope and V) | "fp8" (decode cache)
     B: int
     Hq: int
     Hkv: int
@@ -70,6 +70,12 @@ WORKLOADS = {
     # per-(token, head) fp32 scales, rope 64 in bf16 (one shared k_rope head), V 128 in bf16.
     "mla_prefill_fp8_causal_b1_h128_s8192": Workload(
         name="mla_prefill_fp8_causal_b1_h128_s8192", kind="mla_prefill", seed=5, dtype="fp8+bf16",
+        B=1, Hq=128, Hkv=128, Sq=8192, Skv=8192, D=192, Dv=128, causal=True, Dn=128, Dr=64, Hr=1,
+        scale=1.0 / 192 ** 0.5),
+    # The same MLA prefill with V also in e4m3 (per-(token, head) fp32 value scales), as the
+    # per-token-scale MLA page types V like Q and K_nope.
+    "mla_prefill_fp8v_causal_b1_h128_s8192": Workload(
+        name="mla_prefill_fp8v_causal_b1_h128_s8192", kind="mla_prefill", seed=5, dtype="fp8v",
         B=1, Hq=128, Hkv=128, Sq=8192, Skv=8192, D=192, Dv=128, causal=True, Dn=128, Dr=64, Hr=1,
         scale=1.0 / 192 ** 0.5),
     # Ragged-batch causal prefill: 8 packed sequences with lengths uniform on [512, 3584]
