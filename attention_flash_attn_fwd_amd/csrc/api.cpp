@@ -185,7 +185,7 @@ int mla_decode_fwd(const void* q, const void* kv_cache, void* o, float* lse, con
   if (!q || !o || !kv_lens || (max_kv_len > 0 && !kv_cache)) return ATTN_ERR_NULL;
   if (fp8 && max_kv_len > 0 && !kv_scale) return ATTN_ERR_NULL;
   const fa::SplitPlan p = fa::mla_decode_plan(B, H, max_kv_len);
-  if (B > 65535 || elems({p.n_split, B}) > INT32_MAX) return ATTN_ERR_SHAPE;
+  if (B > 65535 || elems({p.n_split, (B + 7) / 8 * 8}) > INT32_MAX) return ATTN_ERR_SHAPE;
   if (elems({B, H, Dv}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
   const size_t need = fa::decode_workspace_bytes(B, H, Dv, p.n_split);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;

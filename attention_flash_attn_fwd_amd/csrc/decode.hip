@@ -467,6 +467,18 @@ __device__ __forceinline__ uint32_t mla_chunk(uint32_t row, uint32_t lc) {
   return (lc & ~15u) | ((lc & 15u) ^ swz256(row));
 }
 
+// Work item of an MLA split kernel (one workgroup = one split of one sequence).  The grid
+// is 1-D; workgroup i runs on XCD i % 8.  Every split of sequence b runs on XCD b % 8, at
+// consecutive positions there, so the sequence's query rows (147 KiB for 128 heads) come
+// into one L2 once instead of once per split.  Batch entries are padded to a multiple of 8;
+// items past B exit.
+__device__ __forceinline__ bool mla_item(const DecodeArgs& a, int& split, int& b) {
+  const int i = blockIdx.x, x = i & 7, j = i >> 3;
+  split = j % a.n_split;
+  b = x + 8 * (j / a.n_split);
+  return b < a.B;
+}
+
 __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0_raw[MLA_LTILE];
   __shared__ __attribute__((aligned(1024))) char st1_raw[MLA_LTILE];
@@ -474,7 +486,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char xs_raw[MLA_NW * 4096];  // partial S^T per wave
   FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw};
 
-  const int split = blockIdx.x, b = blockIdx.y;
+  int split, b;
+  if (!mla_item(a, split, b)) return;  // uniform over the workgroup
   const int L = min(max(a.kv_lens[b], 0), a.max_len);
   const int start = split * a.chunk;
   if (start >= L) return;  // uniform over the workgroup
@@ -497,8 +510,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
   }
   const char* kv = (const char*)a.k + (size_t)b * a.max_len * MLA_ROWB;
   // direct copy of a tile: LDS byte o = blk*1024 + 16*lane is row o / 1280, physical chunk
-  // (o % 1280) / 16; it receives the logical chunk that maps there (padding slots receive
-  // a duplicate of chunk 71 and are never read)
+  // (o % 1280) / 16; it receives the logical chunk that maps there (padding slots are never
+  // read: their copies take an offset past the buffer's end, which fetches nothing)
   auto issue = [&](int t, FA_LDS char* dst) {
     const int key0 = start + t * TK, valid = min(TK, end - key0);
     const auto r = make_rsrc(kv + (size_t)key0 * MLA_ROWB, (uint32_t)valid * MLA_ROWB);
@@ -506,9 +519,9 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
     for (int i = 0; i < MLA_OPS; i++) {
       const uint32_t blk = i * MLA_NW + wave, o = blk * 1024 + lane * 16;
       const uint32_t row = o / MLA_LROWB, pc = (o % MLA_LROWB) >> 4;
-      const uint32_t lc = min(mla_chunk(row, pc), (uint32_t)(MLA_ROWB / 16 - 1));
+      const uint32_t lc = mla_chunk(row, pc);
       const uint32_t rc = min(row, (uint32_t)(valid - 1));  // rows past the sequence repeat its last row
-      dma16_buf(r, dst + blk * 1024, rc * MLA_ROWB + lc * 16);
+      dma16_buf(r, dst + blk * 1024, lc < MLA_ROWB / 16 ? rc * MLA_ROWB + lc * 16 : kOutOfRange);
     }
   };
   // S^T A operand: key row l32, logical chunk 2(2i + hh) + hl = 4i + 2hh + hl; its XOR part
@@ -669,7 +682,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char dummy_raw[1024];         // target of spare copies
   FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw};
 
-  const int split = blockIdx.x, b = blockIdx.y;
+  int split, b;
+  if (!mla_item(a, split, b)) return;  // uniform over the workgroup
   const int L = min(max(a.kv_lens[b], 0), a.max_len);
   const int start = split * a.chunk;
   if (start >= L) return;  // uniform over the workgroup
@@ -695,8 +709,8 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
   const float* ksb = a.k_scale + (size_t)b * a.max_len;
   // direct copies of a tile: block blk < 18 of LDS bytes [1024 blk, +1024) is row o / 576,
   // physical chunk (o % 576) / 16 for o = 1024 blk + 16 lane; the spare third copy of
-  // wave 2 brings the tile's row scales, the other spares land in a dummy buffer, so every
-  // wave issues the same number of copies per tile
+  // wave 2 brings the tile's row scales, the other spares (offset out of range, so nothing
+  // is fetched) land in a dummy buffer, so every wave issues the same number of copies per tile
   auto issue = [&](int t, FA_LDS char* dst) {
     const int key0 = start + t * TK, valid = min(TK, end - key0);
     const auto r = make_rsrc(kv + (size_t)key0 * M8_ROWB, (uint32_t)valid * M8_ROWB);
@@ -712,7 +726,7 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
         const auto rs = make_rsrc(ksb + key0, (uint32_t)valid * 4);
         dma4_buf(rs, dst + M8_TILE, (uint32_t)min(lane, valid - 1) * 4);
       } else {
-        dma16_buf(r, (FA_LDS char*)dummy_raw, 0);
+        dma16_buf(r, (FA_LDS char*)dummy_raw, kOutOfRange);
       }
     }
   };
@@ -934,7 +948,7 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
 }
 
 hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
-  dim3 grid(a.n_split, a.B);
+  const int grid = a.n_split * ((a.B + 7) / 8 * 8);  // see mla_item
   if (fp8) mla_decode_split_fp8<<<grid, 64 * MLA_NW, 0, s>>>(a);
   else mla_decode_split<<<grid, 64 * MLA_NW, 0, s>>>(a);
   hipError_t e = hipGetLastError();

@@ -150,6 +150,9 @@ __device__ __forceinline__ void dma4(const void* g, FA_LDS char* lds) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// A buffer offset past any range make_rsrc describes: the load fetches nothing from memory
+// (raw buffer loads range-check the offset against the record count).
+constexpr uint32_t kOutOfRange = 0x80000000u;
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, FA_LDS char* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds, 16, voff, 0, 0, 0);
 }
