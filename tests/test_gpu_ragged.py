@@ -46,6 +46,23 @@ def test_varlen_vs_oracle(lq, lk, Hq, Hkv, D, causal):
     assert_lse_close(lse.cpu().numpy(), rl, "LSE")
 
 
+@pytest.mark.parametrize("n_seq", [200, 300])
+def test_varlen_many_sequences(n_seq):
+    """Many short sequences of random lengths (some empty, keys up to two past the queries):
+    most (sequence, head) work items exit at once, the grid covering the longest."""
+    rng = np.random.default_rng(n_seq)
+    lq = rng.integers(0, 40, n_seq)
+    lk = lq + rng.integers(0, 3, n_seq)
+    say(f"case varlen n_seq={n_seq} total_q={lq.sum()} total_k={lk.sum()}")
+    cq, ck = _cu(lq), _cu(lk)
+    q, k, v = _packed(int(cq[-1]), int(ck[-1]), 2, 1, 64)
+    o, lse = fa.prefill_varlen(q, k, v, dev(cq), dev(ck), int(lq.max()), causal=True, scale=0.125, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_varlen(host_f64(q), host_f64(k), host_f64(v), cq, ck, 0.125, True)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+
+
 def test_varlen_equals_fixed_shape_prefill_bitwise():
     """Equal-length sequences: the ragged call computes exactly what the batched call does."""
     B, S, Hq, Hkv, D = 3, 333, 4, 2, 128
