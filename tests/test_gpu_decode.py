@@ -36,6 +36,28 @@ def test_gqa_decode_small(Hq, Hkv):
     _check_gqa(w, lens)
 
 
+def test_decode_lengths_out_of_range_are_clamped():
+    """kv_lens entries below 0 or above max_kv_len are clamped to [0, max_kv_len] in the kernels
+    (the ABI's stated behaviour): the result equals the call with the clamped lengths."""
+    raw = np.array([-5, 1000, 1700, 3, -1], np.int32)
+    clamped = np.clip(raw, 0, 1000)
+    w = workload(GQA, B=len(raw), Hq=8, Hkv=2, Skv=1000)
+    q, k, v, _ = _gqa(w, lens=clamped)
+    o, lse = fa.decode(q, k, v, dev(raw), scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(host_f64(q), host_f64(k), host_f64(v), clamped, w.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "GQA O")
+    assert_lse_close(lse.cpu().numpy(), rl, "GQA LSE")
+    wm = workload(MLA, B=len(raw), Hq=16, Skv=1000)
+    d = make_mla_decode(wm, lens=clamped)
+    qm, kvm = dev_bf16(d["q"]), dev_bf16(d["kv"])
+    om, lm = fa.mla_decode(qm, kvm, dev(raw), dv=512, scale=wm.scale, return_lse=True)
+    torch.cuda.synchronize()
+    rom, rlm = oracle.mla_decode(host_f64(qm), host_f64(kvm), clamped, 512, wm.scale)
+    assert_close(host_f64(om), rom, BF16_TOL, "MLA O")
+    assert_lse_close(lm.cpu().numpy(), rlm, "MLA LSE")
+
+
 def test_gqa_decode_long_single_sequence():
     w = workload(GQA, B=1, Skv=20000)
     _check_gqa(w, [19999])
