@@ -89,6 +89,26 @@ def _need(t: torch.Tensor, name: str, dtypes, ndim: int):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t, name: str, dtype, shape, device):
+    """A caller-supplied output: the kernels write it whole, so it must match exactly."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    return t
+
+
+def _workspace(t, need: int, device):
+    """A caller-supplied workspace of at least `need` bytes; returns (tensor, its size in bytes)."""
+    if t is None:
+        t = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    elif not isinstance(t, torch.Tensor) or not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    return t, t.numel() * t.element_size()
+
+
 _FP8 = (torch.uint8, torch.float8_e4m3fn)
 
 
@@ -101,7 +121,7 @@ def prefill(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     if k.shape[0] != B or k.shape[3] != D or v.shape != k.shape:
         raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
+    o = torch.empty_like(q) if out is None else _out(out, "out", q.dtype, q.shape, q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     dt = ATTN_BF16 if q.dtype == torch.bfloat16 else ATTN_F32
     st = lib().attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), dt, B, Sq, Skv, Hq, Hkv, D,
@@ -122,7 +142,7 @@ def prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causa
     if B < 0 or cu_seqlens_k.shape[0] != B + 1 or k.shape[2] != D or v.shape != k.shape:
         raise ValueError("shape mismatch")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
+    o = torch.empty_like(q) if out is None else _out(out, "out", q.dtype, q.shape, q.device)
     lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device) if return_lse else None
     st = lib().attn_prefill_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
                                        _ptr(cu_seqlens_k), ATTN_BF16, B, Tq, Tk, int(max_seqlen_q), Hq, Hkv, D,
@@ -140,8 +160,8 @@ def merge(o_a, lse_a, o_b, lse_b, out=None, out_lse=None, return_lse: bool = Fal
     B, S, H, D = o_a.shape
     if o_b.shape != o_a.shape or tuple(lse_a.shape) != (B, H, S) or lse_b.shape != lse_a.shape:
         raise ValueError("shape mismatch")
-    o = torch.empty_like(o_a) if out is None else out
-    lse = out_lse
+    o = torch.empty_like(o_a) if out is None else _out(out, "out", o_a.dtype, o_a.shape, o_a.device)
+    lse = None if out_lse is None else _out(out_lse, "out_lse", torch.float32, lse_a.shape, o_a.device)
     if lse is None and return_lse:
         lse = torch.empty_like(lse_a)
     st = lib().attn_merge_fwd(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(o), _ptr(lse),
@@ -176,14 +196,12 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=N
     if k_cache.shape[0] != B or k_cache.shape[3] != D or v_cache.shape != k_cache.shape or kv_lens.shape[0] != B:
         raise ValueError("shape mismatch")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    need = decode_workspace_size(B, Hq, D, Lmax)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q) if out is None else out
+    workspace, ws_bytes = _workspace(workspace, decode_workspace_size(B, Hq, D, Lmax), q.device)
+    o = torch.empty_like(q) if out is None else _out(out, "out", torch.bfloat16, q.shape, q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
     st = lib().attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(kv_lens),
                                _ptr(k_scale), _ptr(v_scale), ATTN_FP8_E4M3 if fp8 else ATTN_BF16,
-                               B, Hq, Hkv, D, Lmax, scale, _ptr(workspace), workspace.numel(), _stream())
+                               B, Hq, Hkv, D, Lmax, scale, _ptr(workspace), ws_bytes, _stream())
     _check("attn_decode_fwd", st)
     return (o, lse) if return_lse else o
 
@@ -218,7 +236,8 @@ def mla_prefill(q_nope, q_rope, k_nope, k_rope, v, q_scale=None, k_scale=None, c
             or tuple(k_rope.shape) != (B, Skv, Hr, Dr) or tuple(v.shape[:3]) != (B, Skv, H)):
         raise ValueError("shape mismatch")
     scale = 1.0 / math.sqrt(Dn + Dr) if scale is None else float(scale)
-    o = torch.empty((B, Sq, H, Dv), dtype=torch.bfloat16, device=v.device) if out is None else out
+    o = (torch.empty((B, Sq, H, Dv), dtype=torch.bfloat16, device=v.device) if out is None
+         else _out(out, "out", torch.bfloat16, (B, Sq, H, Dv), v.device))
     lse = torch.empty((B, H, Sq), dtype=torch.float32, device=v.device) if return_lse else None
     st = lib().mla_prefill_fwd(_ptr(q_nope), _ptr(q_rope), _ptr(k_nope), _ptr(k_rope), _ptr(v), _ptr(o),
                                _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(lse),
@@ -253,14 +272,13 @@ def mla_decode(q, kv_cache, kv_lens, dv: int = 512, scale: float | None = None, 
     if kv_cache.shape[0] != B or kv_cache.shape[2] != Dk or kv_lens.shape[0] != B:
         raise ValueError("shape mismatch")
     scale = 1.0 / math.sqrt(Dk) if scale is None else float(scale)
-    need = mla_decode_workspace_size(B, H, dv, Lmax)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    o = torch.empty((B, H, dv), dtype=torch.bfloat16, device=q.device) if out is None else out
+    workspace, ws_bytes = _workspace(workspace, mla_decode_workspace_size(B, H, dv, Lmax), q.device)
+    o = (torch.empty((B, H, dv), dtype=torch.bfloat16, device=q.device) if out is None
+         else _out(out, "out", torch.bfloat16, (B, H, dv), q.device))
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if return_lse else None
     st = lib().mla_decode_fwd(_ptr(q), _ptr(kv_cache), _ptr(o), _ptr(lse), _ptr(kv_lens), _ptr(kv_scale),
                               ATTN_FP8_E4M3 if fp8 else ATTN_BF16, B, H, Dk, dv, Lmax,
-                              scale, _ptr(workspace), workspace.numel(), _stream())
+                              scale, _ptr(workspace), ws_bytes, _stream())
     _check("mla_decode_fwd", st)
     return (o, lse) if return_lse else o
 
@@ -280,6 +298,8 @@ def quantize_rows_e4m3(x, codes=None, scale=None):
         raise ValueError("codes / scale shape mismatch")
     if codes.dtype not in _FP8 or scale.dtype != torch.float32 or not codes.is_contiguous() or not scale.is_contiguous():
         raise TypeError("codes must be contiguous uint8 / float8_e4m3fn, scale contiguous fp32")
+    if codes.device != x.device or scale.device != x.device:
+        raise ValueError(f"codes / scale must be on {x.device}")
     st = lib().quantize_rows_e4m3(_ptr(x), _ptr(codes), _ptr(scale), n_rows, cols, _stream())
     _check("quantize_rows_e4m3", st)
     return codes, scale

@@ -113,3 +113,26 @@ def test_bf16_causal_full_workload_sampled():
         rlse.append(rl)
     assert_close(np.stack(got), np.stack(ref), BF16_TOL, "O sampled")
     assert_lse_close(np.stack(gl), np.stack(rlse), "LSE sampled")
+
+
+def test_binding_rejects_mismatched_outputs_and_workspaces():
+    """Caller-supplied outputs and workspaces are checked before any launch: a wrong shape,
+    dtype, device or layout raises instead of letting a kernel write past the tensor."""
+    q = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16, device="cuda")
+    for bad in (torch.empty(1, 63, 2, 64, dtype=torch.bfloat16, device="cuda"),
+                torch.empty(1, 64, 2, 64, dtype=torch.float32, device="cuda"),
+                torch.empty(1, 64, 2, 64, dtype=torch.bfloat16),
+                torch.empty(1, 64, 64, 2, dtype=torch.bfloat16, device="cuda").transpose(2, 3)):
+        with pytest.raises((ValueError, TypeError)):
+            fa.prefill(q, q, q, out=bad)
+    qd = torch.zeros(2, 4, 128, dtype=torch.bfloat16, device="cuda")
+    cache = torch.zeros(2, 40, 1, 128, dtype=torch.bfloat16, device="cuda")
+    lens = torch.tensor([40, 3], dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        fa.decode(qd, cache, cache, lens, out=torch.empty(2, 4, 64, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.decode(qd, cache, cache, lens, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    x = torch.zeros(4, 128, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        fa.quantize_rows_e4m3(x, codes=torch.empty(4, 128, dtype=torch.uint8))
+    torch.cuda.synchronize()
