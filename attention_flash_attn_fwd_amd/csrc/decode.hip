@@ -44,7 +44,7 @@ __device__ __forceinline__ bool gqa_item(const DecodeArgs& a, int& kvh, int& spl
 // a load result inside the loop: the only vector-memory waits are the explicit ones, and
 // GQA_NS - 1 tiles stay in flight while a tile is computed.
 
-constexpr int GQA_NS = 3;  // LDS stages per wave
+constexpr int GQA_NS = 4;  // LDS stages per wave
 
 // LDS byte offsets of a 32-key tile of 256-byte rows (bf16 D = 128), 16-byte chunks
 // XOR-permuted by swz16: the direct copy (lane -> row 4i + lane/16), the S^T A operand
