@@ -29,6 +29,7 @@ VARLEN_CASES = [
     ([77, 200], [77, 50], 2, 1, 64),                           # Sq > Skv: leading rows see no key
     ([10, 33], [0, 33], 2, 2, 128),                            # a sequence with no key at all
     ([513, 1000, 7], [513, 1000, 7], 8, 2, 128),
+    ([128, 0, 128, 0, 256], [128, 0, 128, 3, 256], 2, 2, 64),  # sequences of equal work (ties in the work order)
 ]
 
 
