@@ -54,6 +54,10 @@ BF16_CASES = [
     (1, 129, 129, 2, 2, 64, False),
     (1, 129, 129, 4, 1, 64, True),
     (1, 5, 7, 1, 1, 128, True),         # smaller than one tile
+    # causal head dim 128 from 2048 query rows: the 8-wave, 256-row blocks
+    (1, 2100, 2100, 2, 1, 128, True),   # ragged last block, GQA
+    (1, 2048, 2500, 2, 2, 128, True),   # Sq < Skv: bottom-right causal
+    (1, 3000, 2100, 1, 1, 128, True),   # Sq > Skv: leading rows see no key
 ]
 
 
