@@ -337,7 +337,7 @@ def main():
     from workloads.shapes import BENCH_DEFAULT, WORKLOADS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--spinup", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps, so that GPU clocks settle")
