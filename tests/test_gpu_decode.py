@@ -109,7 +109,7 @@ def _mla(w, lens=None):
     return dev_bf16(d["q"]), dev_bf16(d["kv"]), dev(d["kv_lens"])
 
 
-@pytest.mark.parametrize("H", [128, 16, 64])
+@pytest.mark.parametrize("H", [128, 16, 32, 48, 64, 80, 96, 112])
 def test_mla_decode_small(H):
     lens = [1, 33, 300, 0, 128]
     w = workload(MLA, B=len(lens), Hq=H, Skv=300)
@@ -161,6 +161,22 @@ def test_gqa_decode_fp8_small(Hq, Hkv):
     assert_lse_close(lse.cpu().numpy(), rl, "LSE")
 
 
+@pytest.mark.parametrize("G", range(1, 17))
+def test_gqa_decode_every_group_size(G):
+    """Every compiled group size (query heads per kv head, 1..16) over two kv heads, with a
+    bf16 and an e4m3 cache."""
+    lens = [1, 33, 200, 0]
+    _check_gqa(workload(GQA, B=len(lens), Hq=2 * G, Hkv=2, Skv=200), lens)
+    w = workload(GQA8, B=len(lens), Hq=2 * G, Hkv=2, Skv=200)
+    say(f"case gqa decode e4m3 Hq={w.Hq} Hkv={w.Hkv} lens={lens}")
+    (q, k, v, kl, ks, vs), kd, vd = _gqa8(w, lens=lens)
+    o, lse = fa.decode(q, k, v, kl, scale=w.scale, return_lse=True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(host_f64(q), kd, vd, np.asarray(lens), w.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O e4m3")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE e4m3")
+
+
 def test_gqa_decode_fp8_full_workload_sampled():
     w = workload(GQA8)
     say(f"case {w.name} (sampled sequences)")
@@ -200,7 +216,7 @@ def _mla8(w, lens=None):
     return t, oracle.e4m3_to_f64(d["kv"]) * d["kv_scale"][..., None].astype(np.float64)
 
 
-@pytest.mark.parametrize("H", [128, 16, 48, 112])
+@pytest.mark.parametrize("H", [128, 16, 32, 48, 64, 80, 96, 112])
 def test_mla_decode_fp8_small(H):
     lens = [1, 33, 300, 0, 128, 31, 32, 255]
     w = workload(MLA8, B=len(lens), Hq=H, Skv=300)
