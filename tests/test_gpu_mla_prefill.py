@@ -7,7 +7,7 @@ import torch
 import attention_flash_attn_fwd_amd as fa
 import oracle
 from tests.helpers import (BF16_TOL, FP8_TOL, assert_close, assert_lse_close, dev, dev_bf16, host_f64, say)
-from workloads import make_mla_prefill, workload
+from workloads import make_mla_prefill, quantize_rows_e4m3, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +69,29 @@ def test_mla_prefill_bf16_nope_without_scales():
     ro, _ = oracle.mla_prefill(host_f64(qn), host_f64(qr), host_f64(kn), host_f64(kr), host_f64(v), ones, ones,
                                w.scale, True)
     assert_close(host_f64(o), ro, BF16_TOL, "O")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_mla_prefill_bf16_nope_with_scales_and_e4m3_v(causal):
+    """bf16 nope operands with per-token q/k scales, one k_rope head per query head, and an
+    e4m3 V with one fp32 scale per (token, head) row."""
+    S, H = 170, 2
+    rng = np.random.default_rng(12)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    bf = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    qn, kn, qr, kr = bf(f(1, S, H, 128)), bf(f(1, S, H, 128)), bf(f(1, S, H, 64)), bf(f(1, S, H, 64))
+    qs = rng.uniform(0.5, 2.0, (1, S, H)).astype(np.float32)
+    ks = rng.uniform(0.5, 2.0, (1, S, H)).astype(np.float32)
+    codes, vs = quantize_rows_e4m3(f(1, S, H, 128))
+    scale = 192 ** -0.5
+    say(f"case mla prefill bf16 nope + scales, e4m3 V, S={S} H={H} Hr={H} causal={causal}")
+    o, lse = fa.mla_prefill(qn, qr, kn, kr, dev(codes), dev(qs), dev(ks), causal=causal, scale=scale,
+                            return_lse=True, v_scale=dev(vs))
+    torch.cuda.synchronize()
+    vd = oracle.e4m3_to_f64(codes) * vs[..., None].astype(np.float64)
+    ro, rl = oracle.mla_prefill(host_f64(qn), host_f64(qr), host_f64(kn), host_f64(kr), vd, qs, ks, scale, causal)
+    assert_close(host_f64(o), ro, FP8_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
 
 
 @pytest.mark.parametrize("name", [MLA, MLA8V])
