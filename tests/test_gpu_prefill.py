@@ -58,6 +58,9 @@ BF16_CASES = [
     (1, 2100, 2100, 2, 1, 128, True),   # ragged last block, GQA
     (1, 2048, 2500, 2, 2, 128, True),   # Sq < Skv: bottom-right causal
     (1, 3000, 2100, 1, 1, 128, True),   # Sq > Skv: leading rows see no key
+    (2, 2100, 2100, 6, 2, 128, True),   # 8-wave blocks, two sequences, group of 3
+    (2, 100, 300, 6, 2, 64, True),      # head dim 64, Sq < Skv, group of 3
+    (1, 300, 100, 3, 3, 64, True),      # head dim 64, Sq > Skv
 ]
 
 
