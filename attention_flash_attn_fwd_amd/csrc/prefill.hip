@@ -1,5 +1,6 @@
 // Prefill forward kernels on bf16 matrix cores: MHA / GQA (bf16 q/k/v) and MLA with
-// per-token scales (e4m3 or bf16 nope part, bf16 rope part, bf16 V).
+// per-token scales (e4m3 or bf16 nope part, bf16 rope part, bf16 V or e4m3 V with per-row
+// scales).
 //
 // Method: the flash-attention forward that Modular's "KVPipelineGeneric" page describes
 // (S = Q.K' and O += P.V per K/V tile over a pipeline of K/V stages), with the online
@@ -13,8 +14,9 @@
 //
 // Workgroup: NW waves, query blocks of 32 * NW rows (32 per wave), K/V tiles of BN = 64
 // keys; NW = 4 (two workgroups per CU), or 8 (one workgroup per CU, sharing each K/V tile
-// between twice the rows) for long causal bf16 prefills of head dim 128.  Causal workgroups take a pair of query blocks (i, n-1-i), so every workgroup has
-// the same number of key tiles; workgroups are ordered head-major within each XCD (the
+// between twice the rows) for long causal bf16 prefills of head dim 128.  Causal
+// workgroups take a pair of query blocks (i, n-1-i), so every workgroup has the same
+// number of key tiles; workgroups are ordered head-major within each XCD (the
 // dispatcher deals workgroups to the 8 XCDs round-robin), so the workgroups of one
 // (batch, head) run together and share its K/V through that XCD's L2.
 #include "device.h"
