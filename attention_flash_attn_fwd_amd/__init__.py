@@ -25,7 +25,7 @@ EXPORTS = {
     "attn_prefill_varlen_fwd": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 9 +
                                 [ctypes.c_float, ctypes.c_void_p]),
     "attn_merge_fwd": (ctypes.c_int, [ctypes.c_void_p] * 6 + [ctypes.c_int] * 5 + [ctypes.c_void_p]),
-    "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 5),
     "attn_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "mla_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int] * 11 +
@@ -170,8 +170,8 @@ def merge(o_a, lse_a, o_b, lse_b, out=None, out_lse=None, return_lse: bool = Fal
     return (o, lse) if (return_lse or out_lse is not None) else o
 
 
-def decode_workspace_size(B: int, Hq: int, D: int, max_kv_len: int) -> int:
-    return int(lib().attn_decode_workspace_size(B, Hq, D, max_kv_len))
+def decode_workspace_size(B: int, Hq: int, Hkv: int, D: int, max_kv_len: int) -> int:
+    return int(lib().attn_decode_workspace_size(B, Hq, Hkv, D, max_kv_len))
 
 
 def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=None, out=None,
@@ -196,7 +196,7 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=N
     if k_cache.shape[0] != B or k_cache.shape[3] != D or v_cache.shape != k_cache.shape or kv_lens.shape[0] != B:
         raise ValueError("shape mismatch")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    workspace, ws_bytes = _workspace(workspace, decode_workspace_size(B, Hq, D, Lmax), q.device)
+    workspace, ws_bytes = _workspace(workspace, decode_workspace_size(B, Hq, Hkv, D, Lmax), q.device)
     o = torch.empty_like(q) if out is None else _out(out, "out", torch.bfloat16, q.shape, q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if return_lse else None
     st = lib().attn_decode_fwd(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(kv_lens),

@@ -103,9 +103,9 @@ int attn_merge_fwd(const void* o_a, const float* lse_a, const void* o_b, const f
   return hip_status(fa::launch_merge(a, dtype == ATTN_BF16, stream));
 }
 
-size_t attn_decode_workspace_size(int B, int Hq, int D, int max_kv_len) {
-  if (B < 0 || Hq <= 0 || D <= 0 || max_kv_len < 0) return 0;
-  const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0) return 0;
+  const fa::SplitPlan p = fa::gqa_decode_plan(B, Hkv, max_kv_len);
   return fa::decode_workspace_bytes(B, Hq, D, p.n_split);
 }
 
@@ -118,12 +118,12 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
   if (!fp8 && (k_scale || v_scale)) return ATTN_ERR_DTYPE;  // scales belong to e4m3 caches only
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (elems({B, max_kv_len, Hkv, D}) < 0 || elems({B, Hq, D}) < 0) return ATTN_ERR_SHAPE;
-  if (D != 128 || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((D != 64 && D != 128) || Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
   if (bad_scale(softmax_scale)) return ATTN_ERR_SCALE;
   if (B == 0) return ATTN_OK;
   if (!q || !o || !kv_lens || (max_kv_len > 0 && (!k_cache || !v_cache))) return ATTN_ERR_NULL;
   if (fp8 && max_kv_len > 0 && (!k_scale || !v_scale)) return ATTN_ERR_NULL;
-  const fa::SplitPlan p = fa::gqa_decode_plan(B, Hq, max_kv_len);
+  const fa::SplitPlan p = fa::gqa_decode_plan(B, Hkv, max_kv_len);
   if (B > 65535 || p.n_split > 65535 || elems({p.n_split, Hkv, (B + 7) / 8 * 8}) > INT32_MAX) return ATTN_ERR_SHAPE;
   if (elems({B, Hq, D}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
   const size_t need = fa::decode_workspace_bytes(B, Hq, D, p.n_split);
@@ -136,7 +136,7 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_kv_len;
   a.n_split = p.n_split; a.chunk = p.chunk;
   a.scale = softmax_scale;
-  return hip_status(fa::launch_gqa_decode(a, fp8, stream));
+  return hip_status(fa::launch_gqa_decode(a, D, fp8, stream));
 }
 
 int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope, const void* k_rope, const void* v,

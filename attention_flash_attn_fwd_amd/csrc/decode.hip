@@ -18,7 +18,7 @@
 namespace fa {
 namespace {
 
-constexpr int TK = 32;  // keys per tile
+constexpr int TK = kDecodeTileKeys;  // keys per tile
 
 // Work item of a GQA split kernel (one wave = one split of one (batch, kv head)).  The grid
 // is 1-D; workgroup i runs on XCD i % 8.  The Hkv waves of one (split, batch) pair take
@@ -42,20 +42,48 @@ __device__ __forceinline__ bool gqa_item(const DecodeArgs& a, int& kvh, int& spl
 // barriers: the wave is alone in its workgroup).  Every LDS read of a tile is an asm block
 // that waits for itself (lds_* in device.h), so no instruction the compiler sees consumes
 // a load result inside the loop: the only vector-memory waits are the explicit ones, and
-// GQA_NS - 1 tiles stay in flight while a tile is computed.
+// GQA_NS - 1 tiles stay in flight while a tile is computed.  While fewer than GQA_NS - 1
+// tiles are left, each step issues the same number of copies into a spare LDS block that
+// is never read, at an offset past every buffer (they fetch nothing), so the wait count is
+// the same on every path and no copy is ever in flight into a stage being read.
+// Head dim D = 128 or 64.
 
 constexpr int GQA_NS = 4;  // LDS stages per wave
 
-// LDS byte offsets of a 32-key tile of 256-byte rows (bf16 D = 128), 16-byte chunks
-// XOR-permuted by swz16: the direct copy (lane -> row 4i + lane/16), the S^T A operand
-// (row 16kb + l16, chunk 4cc + g) and the transposed V reads (see below).
-template <int G>
+// 16-byte chunk swizzles of the GQA tiles not covered by device.h:
+//  * bf16 rows of 128 bytes (D = 64) alternate bank halves by parity.  With t = (row / 2) % 8,
+//    the 16 rows of an S^T A-operand read need an XOR one-to-one over t, and the 8 rows read
+//    together by a transposing V read (32 lanes: rows 8k .. 8k+7) need distinct chunk pairs
+//    (xor >> 1) over t % 4 within each parity: ((t % 4) << 1) | (t / 4) is both.
+//  * e4m3 rows of 64 bytes (D = 64) put four rows in a bank row.  The 16 rows of an S^T read
+//    (rows 16kb .. 16kb+15) and the 16 rows of a transposing V read pass (row / 4 in {0, 1, 4, 5}
+//    or {2, 3, 6, 7}) both need an XOR one-to-one over row / 4 within each class of row % 4:
+//    ((row / 4) % 4) ^ (2 * ((row / 16) % 2)) is.
+__device__ __forceinline__ uint32_t swz_b64(uint32_t row) {
+  const uint32_t t = (row >> 1) & 7u;
+  return ((t & 3u) << 1) | (t >> 2);
+}
+__device__ __forceinline__ uint32_t swz_q64(uint32_t row) { return ((row >> 2) & 3u) ^ ((row >> 3) & 2u); }
+
+template <int D>
+__device__ __forceinline__ uint32_t gqa_swz_bf16(uint32_t row) {
+  return D == 128 ? swz16(row) : swz_b64(row);
+}
+
+template <int D, int G>
 __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
-  constexpr int D = 128, ROWB = 256, TILE = TK * ROWB;  // 8 KiB per K or V tile
-  constexpr int STAGE = 2 * TILE;                       // K tile | V tile
-  constexpr int OPS = STAGE / 1024;                     // direct copies per tile (16)
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int ROWB = 2 * D, TILE = TK * ROWB;     // K or V tile: 8 KiB (D = 128), 4 KiB (D = 64)
+  constexpr int STAGE = 2 * TILE;                   // K tile | V tile
+  constexpr int NCP = TILE / 1024;                  // direct copies per K or V tile
+  constexpr int OPS = 2 * NCP;                      // direct copies per tile
+  constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16; // rows per copy instruction, chunks per row
+  constexpr int NC = D / 32;                        // S^T contraction steps
+  constexpr int NB = D / 16;                        // 16-column blocks of O^T
   __shared__ __attribute__((aligned(1024))) char ring_raw[GQA_NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char spare_raw[1024];
   FA_LDS char* const ring = (FA_LDS char*)ring_raw;
+  FA_LDS char* const spare = (FA_LDS char*)spare_raw;
 
   int kvh, split, b;
   if (!gqa_item(a, kvh, split, b)) return;
@@ -71,44 +99,44 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 
   // Q^T as the B operand: column l16 = query head kvh*G + l16 (zero past the group),
   // k = head-dim 32cc + 8g .. +7
-  i32x4_t qf[D / 32];
+  i32x4_t qf[NC];
   {
     const int hq = kvh * G + (l16 < G ? l16 : 0);
     const char* qp = (const char*)a.q + ((size_t)b * a.Hq + hq) * ROWB;
 #pragma unroll
-    for (int cc = 0; cc < D / 32; cc++) {
+    for (int cc = 0; cc < NC; cc++) {
       const i32x4_t x = *(const i32x4_t*)(qp + cc * 64 + g * 16);
       qf[cc] = l16 < G ? x : i32x4_t{};
     }
   }
   const char* kbase = (const char*)a.k + ((size_t)b * a.max_len * a.Hkv + kvh) * ROWB;
   const char* vbase = (const char*)a.v + ((size_t)b * a.max_len * a.Hkv + kvh) * ROWB;
-  // direct copy: LDS row 4i + g holds key row 4i + g with 16-byte chunks XOR-permuted
-  uint32_t coff[TILE / 1024];
+  // direct copy: LDS row RPI*i + lane/CPR holds that key row with its 16-byte chunks
+  // XOR-permuted
+  uint32_t coff[NCP];
 #pragma unroll
-  for (int i = 0; i < TILE / 1024; i++) {
-    const uint32_t row = 4 * i + g;
-    coff[i] = row * rstride + ((l16 ^ swz16(row)) << 4);
+  for (int i = 0; i < NCP; i++) {
+    const uint32_t row = RPI * i + lane / CPR;
+    coff[i] = row * rstride + (((lane % CPR) ^ gqa_swz_bf16<D>(row)) << 4);
   }
   // S^T A operand of key block kb, step cc: row 16kb + l16, chunk 4cc + g
-  uint32_t ka[8];
+  uint32_t ka[2 * NC];
 #pragma unroll
   for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-    for (int cc = 0; cc < 4; cc++) {
+    for (int cc = 0; cc < NC; cc++) {
       const uint32_t row = 16 * kb + l16;
-      ka[4 * kb + cc] = row * ROWB + (((4 * cc + g) ^ swz16(row)) << 4);
+      ka[NC * kb + cc] = row * ROWB + (((4 * cc + g) ^ gqa_swz_bf16<D>(row)) << 4);
     }
-  // transposing V reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4) .. +3.  The column
-  // slab of block db is chunk pair db: swizzled to pair db ^ (swz >> 1), chunk (l16%4)/2 of
-  // the pair flipped by swz & 1.
-  uint32_t va[D / 16][2];
+  // transposing V reads: rows 16u + 4g + l16/4, columns 16db + 4(l16%4) .. +3, i.e. chunk
+  // 2db + (l16%4)/2 of the row (before the XOR), byte 8(l16%2) of the chunk
+  uint32_t va[NB][2];
 #pragma unroll
   for (int u = 0; u < 2; u++) {
-    const uint32_t row = 16 * u + 4 * g + (l16 >> 2), sw = swz16(row);
-    const uint32_t base = TILE + row * ROWB + (((((l16 & 3) >> 1) ^ (sw & 1))) << 4) + ((l16 & 1) << 3);
+    const uint32_t row = 16 * u + 4 * g + (l16 >> 2), sw = gqa_swz_bf16<D>(row);
 #pragma unroll
-    for (int db = 0; db < D / 16; db++) va[db][u] = base + ((db ^ (sw >> 1)) << 5);
+    for (int db = 0; db < NB; db++)
+      va[db][u] = TILE + row * ROWB + (((2 * db + ((l16 & 3) >> 1)) ^ sw) << 4) + ((l16 & 1) << 3);
   }
 
   // tile t -> stage t % GQA_NS; rows past the sequence repeat its last row (masked below)
@@ -120,50 +148,59 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
     const auto rv = make_rsrc(vbase + (size_t)key0 * rstride, bytes);
     if (valid == TK) {
 #pragma unroll
-      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rk, dst + i * 1024, coff[i]);
+      for (int i = 0; i < NCP; i++) dma16_buf(rk, dst + i * 1024, coff[i]);
 #pragma unroll
-      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rv, dst + TILE + i * 1024, coff[i]);
+      for (int i = 0; i < NCP; i++) dma16_buf(rv, dst + TILE + i * 1024, coff[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < TILE / 1024; i++) {
-        const uint32_t row = 4 * i + g, rc = min(row, (uint32_t)(valid - 1));
-        const uint32_t off = rc * rstride + ((l16 ^ swz16(row)) << 4);
+      for (int i = 0; i < NCP; i++) {
+        const uint32_t row = RPI * i + lane / CPR, rc = min(row, (uint32_t)(valid - 1));
+        const uint32_t off = rc * rstride + (((lane % CPR) ^ gqa_swz_bf16<D>(row)) << 4);
         dma16_buf(rk, dst + i * 1024, off);
         dma16_buf(rv, dst + TILE + i * 1024, off);
       }
     }
   };
+  auto issue_spare = [&]() {
+    const auto r = make_rsrc(kbase, ROWB);
+#pragma unroll
+    for (int i = 0; i < OPS; i++) dma16_buf(r, spare, kOutOfRange);
+  };
 
   float m_ref = -INFINITY, neg = 0.f, l = 0.f;
-  f32x4_t o[D / 16];
+  f32x4_t o[NB];
 #pragma unroll
-  for (int d = 0; d < D / 16; d++) o[d] = f32x4_t{};
+  for (int d = 0; d < NB; d++) o[d] = f32x4_t{};
 
-  // prologue: tiles 0 .. GQA_NS-2.  Every tile then issues tile t + GQA_NS - 1 (past the
-  // end, a repeat of the last tile: an L2 hit, never read), so exactly GQA_NS - 1 tiles
-  // of copies are younger than tile t's and the wait count is the same on every path.
+  // prologue: tiles 0 .. GQA_NS-2; then every step issues tile t + GQA_NS - 1 (or spare
+  // copies), so exactly GQA_NS - 1 tiles of copies are younger than tile t's
 #pragma unroll
-  for (int p = 0; p < GQA_NS - 1; p++) issue(min(p, n_tiles - 1));
+  for (int p = 0; p < GQA_NS - 1; p++) {
+    if (p < n_tiles) issue(p);
+    else issue_spare();
+  }
   for (int t = 0; t < n_tiles; t++) {
     // the stage refilled here held tile t - 1, whose reads completed in their asm blocks
-    issue(min(t + GQA_NS - 1, n_tiles - 1));
+    if (t + GQA_NS - 1 < n_tiles) issue(t + GQA_NS - 1);
+    else issue_spare();
     wait_vmcnt<(GQA_NS - 1) * OPS>();
     asm volatile("" ::: "memory");
     const uint32_t st = lds_addr(ring) + (t % GQA_NS) * STAGE;
 
-    i32x4_t kf[8];
+    i32x4_t kf[2 * NC];
     {
-      uint32_t ad[8];
+      uint32_t ad[2 * NC];
 #pragma unroll
-      for (int i = 0; i < 8; i++) ad[i] = st + ka[i];
-      lds_b128_x8(kf, ad);
+      for (int i = 0; i < 2 * NC; i++) ad[i] = st + ka[i];
+      if constexpr (NC == 4) lds_b128_x8(kf, ad);
+      else lds_b128_x4(kf, ad);
     }
     f32x4_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
       s[kb] = f32x4_t{};
 #pragma unroll
-      for (int cc = 0; cc < D / 32; cc++) s[kb] = mfma16x16x32_bf16(kf[4 * kb + cc], qf[cc], s[kb]);
+      for (int cc = 0; cc < NC; cc++) s[kb] = mfma16x16x32_bf16(kf[NC * kb + cc], qf[cc], s[kb]);
     }
     const int key0 = start + t * TK;
     if (key0 + TK > end) {
@@ -182,7 +219,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
       const float alpha = exp2_fast((m_ref - m_use) * c);
       l *= alpha;
 #pragma unroll
-      for (int d = 0; d < D / 16; d++) o[d] *= alpha;
+      for (int d = 0; d < NB; d++) o[d] *= alpha;
       m_ref = m_new;
       neg = -m_use * c;
     }
@@ -195,7 +232,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; i++) l = dot2_bf16(pb[i], kBf16PairOne, l);
 #pragma unroll
-    for (int half = 0; half < 2; half++) {
+    for (int half = 0; half < NB / 4; half++) {
       uint32_t ad[8];
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -209,7 +246,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
         o[4 * half + j] = mfma16x16x32_bf16(cat(vr[2 * j], vr[2 * j + 1]), pb, o[4 * half + j]);
     }
   }
-  wait_vmcnt<0>();  // the repeat copies past the end land before the LDS is released
+  wait_vmcnt<0>();  // the spare copies land before the LDS is released
 
   const float l_tot = xor32_sum(xor16_sum(l));
   if (l16 < G) {
@@ -217,7 +254,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
     const size_t pidx = ((size_t)b * a.Hq + hq) * a.n_split + split;
     float* po = a.part_o + pidx * D;
 #pragma unroll
-    for (int db = 0; db < D / 16; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
+    for (int db = 0; db < NB; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
     if (g == 0) {
       a.part_ml[2 * pidx] = m_ref;
       a.part_ml[2 * pidx + 1] = l_tot;
@@ -228,23 +265,39 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
 // ------------------------------------------------------------------------------------
 // GQA decode split over an e4m3 cache with per-token scales (k_scale, v_scale per key row
 // and kv head).  Same structure as the bf16 kernel, at half the bytes per key:
-//  * K codes (128-byte rows) go through the LDS ring; the contraction order is permuted so
-//    that a lane's four K fragments are one contiguous 32-byte run of its key row (step cc,
-//    lane group g, element i covers head dim 32g + 8cc + i; Q^T uses the same order), and
-//    e4m3 -> bf16 is exact, so S^T = K_code.Q^T runs on the bf16 matrix cores and the key
-//    scale multiplies S afterwards;
+//  * K codes go through the LDS ring; the contraction order is permuted so that a lane's K
+//    fragments are one contiguous run of its key row (step cc, lane group g, element i covers
+//    head dim (D/4)g + 8cc + i; Q^T uses the same order), and e4m3 -> bf16 is exact, so
+//    S^T = K_code.Q^T runs on the bf16 matrix cores and the key scale multiplies S afterwards;
 //  * V codes are read transposed one byte wide (ds_read_b64_tr_b8: 8 keys of one column per
 //    lane, one read per product instead of two), converted exactly, and the value scale is
 //    folded into P: O += (P . v_scale) V_code.
 
-template <int G>
+template <int D>
+__device__ __forceinline__ uint32_t gqa_swz_k8(uint32_t row) {
+  return D == 128 ? swz_half(row) : swz_q64(row);
+}
+template <int D>
+__device__ __forceinline__ uint32_t gqa_swz_v8(uint32_t row) {
+  return D == 128 ? swz_fp8v(row) : swz_q64(row);
+}
+
+template <int D, int G>
 __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
-  constexpr int D = 128, ROWB = 128, TILE = TK * ROWB;  // 4 KiB per K or V tile
-  constexpr int SCB = 256;                              // one scale copy: 64 lanes x 4 bytes
-  constexpr int STAGE = 2 * TILE + 2 * SCB;             // K codes | V codes | k_scale | v_scale
-  constexpr int OPS = 2 * TILE / 1024 + 2;              // direct copies per tile (10)
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int ROWB = D, TILE = TK * ROWB;         // 4 KiB (D = 128), 2 KiB (D = 64) per K or V tile
+  constexpr int SCB = 256;                          // one scale copy: 64 lanes x 4 bytes
+  constexpr int STAGE = 2 * TILE + 2 * SCB;         // K codes | V codes | k_scale | v_scale
+  constexpr int NCP = TILE / 1024;                  // direct copies per K or V tile
+  constexpr int OPS = 2 * NCP + 2;                  // direct copies per tile
+  constexpr int RPI = 1024 / ROWB, CPR = ROWB / 16; // rows per copy instruction, chunks per row
+  constexpr int KCH = D / 64;                       // 16-byte K reads per lane per 16-key block
+  constexpr int NC = D / 32;                        // S^T contraction steps
+  constexpr int NB = D / 16;                        // 16-column blocks of O^T
   __shared__ __attribute__((aligned(1024))) char ring_raw[GQA_NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char spare_raw[1024];
   FA_LDS char* const ring = (FA_LDS char*)ring_raw;
+  FA_LDS char* const spare = (FA_LDS char*)spare_raw;
 
   int kvh, split, b;
   if (!gqa_item(a, kvh, split, b)) return;
@@ -260,14 +313,14 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
   const uint32_t sstride = (uint32_t)a.Hkv * 4;     // scale bytes between consecutive keys
 
   // Q^T as the B operand: column l16 = query head kvh*G + l16 (zero past the group); step cc
-  // holds head dims 32g + 8cc .. +7
-  i32x4_t qf[D / 32];
+  // holds head dims (D/4)g + 8cc .. +7
+  i32x4_t qf[NC];
   {
     const int hq = kvh * G + (l16 < G ? l16 : 0);
     const char* qp = (const char*)a.q + ((size_t)b * a.Hq + hq) * (D * 2);
 #pragma unroll
-    for (int cc = 0; cc < D / 32; cc++) {
-      const i32x4_t x = *(const i32x4_t*)(qp + (32 * g + 8 * cc) * 2);
+    for (int cc = 0; cc < NC; cc++) {
+      const i32x4_t x = *(const i32x4_t*)(qp + ((D / 4) * g + 8 * cc) * 2);
       qf[cc] = l16 < G ? x : i32x4_t{};
     }
   }
@@ -276,33 +329,33 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
   const char* vbase = (const char*)a.v + row0 * ROWB;
   const float* ksbase = a.k_scale + row0;
   const float* vsbase = a.v_scale + row0;
-  // direct copies: LDS row 8i + lane/8 holds key row 8i + lane/8, its 16-byte chunks
-  // XOR-permuted by swz_half (K) and swz_fp8v (V)
-  uint32_t kcoff[TILE / 1024], vcoff[TILE / 1024];
+  // direct copies: LDS row RPI*i + lane/CPR holds that key row, its 16-byte chunks
+  // XOR-permuted by the K and V swizzles
+  uint32_t kcoff[NCP], vcoff[NCP];
 #pragma unroll
-  for (int i = 0; i < TILE / 1024; i++) {
-    const uint32_t row = 8 * i + lane / 8;
-    kcoff[i] = row * rstride + (((lane & 7) ^ swz_half(row)) << 4);
-    vcoff[i] = row * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4);
+  for (int i = 0; i < NCP; i++) {
+    const uint32_t row = RPI * i + lane / CPR;
+    kcoff[i] = row * rstride + (((lane % CPR) ^ gqa_swz_k8<D>(row)) << 4);
+    vcoff[i] = row * rstride + (((lane % CPR) ^ gqa_swz_v8<D>(row)) << 4);
   }
-  // K fragments: key row 16kb + l16, bytes 32g + 16hh .. +15 (chunk 2g + hh)
-  uint32_t ka[4];
+  // K fragments: key row 16kb + l16, bytes (D/4)g + 16hh .. +15 (chunk KCH*g + hh)
+  uint32_t ka[2 * KCH];
 #pragma unroll
   for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-    for (int hh = 0; hh < 2; hh++) {
+    for (int hh = 0; hh < KCH; hh++) {
       const uint32_t row = 16 * kb + l16;
-      ka[2 * kb + hh] = row * ROWB + (((2 * g + hh) ^ swz_half(row)) << 4);
+      ka[KCH * kb + hh] = row * ROWB + (((KCH * g + hh) ^ gqa_swz_k8<D>(row)) << 4);
     }
   // transposing V reads: lane 2e + h of group g reads key row R = 16(e/4) + 4g + e%4 at
   // byte 8h of column chunk db, so output byte e of lane l is column 16db + l%16 of key R --
   // the key order in which P^T is packed below
-  uint32_t va[D / 16];
+  uint32_t va[NB];
   {
     const uint32_t e = (lane & 15) >> 1, h = lane & 1;
     const uint32_t row = 16 * (e >> 2) + 4 * g + (e & 3);
 #pragma unroll
-    for (int db = 0; db < D / 16; db++) va[db] = TILE + row * ROWB + 8 * h + ((db ^ swz_fp8v(row)) << 4);
+    for (int db = 0; db < NB; db++) va[db] = TILE + row * ROWB + 8 * h + ((db ^ gqa_swz_v8<D>(row)) << 4);
   }
   // scales of the tile's keys: register v of block kb holds key 16kb + 4g + v
   const uint32_t g16 = 16u * g;
@@ -316,15 +369,15 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
     const auto rv = make_rsrc(vbase + (size_t)key0 * rstride, bytes);
     if (valid == TK) {
 #pragma unroll
-      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rk, dst + i * 1024, kcoff[i]);
+      for (int i = 0; i < NCP; i++) dma16_buf(rk, dst + i * 1024, kcoff[i]);
 #pragma unroll
-      for (int i = 0; i < TILE / 1024; i++) dma16_buf(rv, dst + TILE + i * 1024, vcoff[i]);
+      for (int i = 0; i < NCP; i++) dma16_buf(rv, dst + TILE + i * 1024, vcoff[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < TILE / 1024; i++) {
-        const uint32_t row = 8 * i + lane / 8, rc = min(row, (uint32_t)(valid - 1));
-        dma16_buf(rk, dst + i * 1024, rc * rstride + (((lane & 7) ^ swz_half(row)) << 4));
-        dma16_buf(rv, dst + TILE + i * 1024, rc * rstride + (((lane & 7) ^ swz_fp8v(row)) << 4));
+      for (int i = 0; i < NCP; i++) {
+        const uint32_t row = RPI * i + lane / CPR, rc = min(row, (uint32_t)(valid - 1));
+        dma16_buf(rk, dst + i * 1024, rc * rstride + (((lane % CPR) ^ gqa_swz_k8<D>(row)) << 4));
+        dma16_buf(rv, dst + TILE + i * 1024, rc * rstride + (((lane % CPR) ^ gqa_swz_v8<D>(row)) << 4));
       }
     }
     // scales of keys key0 + lane (lanes past the tile repeat its last key)
@@ -333,44 +386,53 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
     dma4_buf(make_rsrc(ksbase + (size_t)key0 * a.Hkv, sbytes), dst + 2 * TILE, so);
     dma4_buf(make_rsrc(vsbase + (size_t)key0 * a.Hkv, sbytes), dst + 2 * TILE + SCB, so);
   };
+  auto issue_spare = [&]() {
+    const auto r = make_rsrc(kbase, ROWB);
+#pragma unroll
+    for (int i = 0; i < OPS; i++) dma16_buf(r, spare, kOutOfRange);
+  };
 
   float m_ref = -INFINITY, neg = 0.f, l = 0.f;
-  f32x4_t o[D / 16];
+  f32x4_t o[NB];
 #pragma unroll
-  for (int d = 0; d < D / 16; d++) o[d] = f32x4_t{};
+  for (int d = 0; d < NB; d++) o[d] = f32x4_t{};
 
   // same ring discipline as the bf16 kernel: GQA_NS - 1 tiles of copies in flight
 #pragma unroll
-  for (int p = 0; p < GQA_NS - 1; p++) issue(min(p, n_tiles - 1));
+  for (int p = 0; p < GQA_NS - 1; p++) {
+    if (p < n_tiles) issue(p);
+    else issue_spare();
+  }
   for (int t = 0; t < n_tiles; t++) {
-    issue(min(t + GQA_NS - 1, n_tiles - 1));
+    if (t + GQA_NS - 1 < n_tiles) issue(t + GQA_NS - 1);
+    else issue_spare();
     wait_vmcnt<(GQA_NS - 1) * OPS>();
     asm volatile("" ::: "memory");
     const uint32_t st = lds_addr(ring) + (t % GQA_NS) * STAGE;
 
-    i32x4_t kf[4], sc[4];
+    i32x4_t kf[2 * KCH], sc[4];
     {
-      uint32_t ad[8];
+      constexpr int NR = 2 * KCH + 4;
+      uint32_t ad[NR];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        ad[i] = st + ka[i];
-        ad[4 + i] = st + sa[i];
-      }
-      i32x4_t r[8];
-      lds_b128_x8(r, ad);
+      for (int i = 0; i < 2 * KCH; i++) ad[i] = st + ka[i];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        kf[i] = r[i];
-        sc[i] = r[4 + i];
-      }
+      for (int i = 0; i < 4; i++) ad[2 * KCH + i] = st + sa[i];
+      i32x4_t r[NR];
+      if constexpr (NR == 8) lds_b128_x8(r, ad);
+      else lds_b128_x6(r, ad);
+#pragma unroll
+      for (int i = 0; i < 2 * KCH; i++) kf[i] = r[i];
+#pragma unroll
+      for (int i = 0; i < 4; i++) sc[i] = r[2 * KCH + i];
     }
     f32x4_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; kb++) {
       s[kb] = f32x4_t{};
 #pragma unroll
-      for (int hh = 0; hh < 2; hh++) {
-        const i32x4_t w = kf[2 * kb + hh];
+      for (int hh = 0; hh < KCH; hh++) {
+        const i32x4_t w = kf[KCH * kb + hh];
         s[kb] = mfma16x16x32_bf16(e4m3x8_to_bf16(i32x2_t{w.x, w.y}), qf[2 * hh], s[kb]);
         s[kb] = mfma16x16x32_bf16(e4m3x8_to_bf16(i32x2_t{w.z, w.w}), qf[2 * hh + 1], s[kb]);
       }
@@ -399,7 +461,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
       const float alpha = exp2_fast((m_ref - m_use) * c);
       l *= alpha;
 #pragma unroll
-      for (int d = 0; d < D / 16; d++) o[d] *= alpha;
+      for (int d = 0; d < NB; d++) o[d] *= alpha;
       m_ref = m_new;
       neg = -m_use * c;
     }
@@ -413,17 +475,18 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
       }
     const i32x4_t pb = {pack_bf16(e[0] * vs0[0], e[1] * vs0[1]), pack_bf16(e[2] * vs0[2], e[3] * vs0[3]),
                         pack_bf16(e[4] * vs1[0], e[5] * vs1[1]), pack_bf16(e[6] * vs1[2], e[7] * vs1[3])};
-    i32x2_t vr[D / 16];
+    i32x2_t vr[NB];
     {
-      uint32_t ad[D / 16];
+      uint32_t ad[NB];
 #pragma unroll
-      for (int db = 0; db < D / 16; db++) ad[db] = st + va[db];
-      lds_tr8_x8(vr, ad);
+      for (int db = 0; db < NB; db++) ad[db] = st + va[db];
+      if constexpr (NB == 8) lds_tr8_x8(vr, ad);
+      else lds_tr8_x4(vr, ad);
     }
 #pragma unroll
-    for (int db = 0; db < D / 16; db++) o[db] = mfma16x16x32_bf16(e4m3x8_to_bf16(vr[db]), pb, o[db]);
+    for (int db = 0; db < NB; db++) o[db] = mfma16x16x32_bf16(e4m3x8_to_bf16(vr[db]), pb, o[db]);
   }
-  wait_vmcnt<0>();  // the repeat copies past the end land before the LDS is released
+  wait_vmcnt<0>();  // the spare copies land before the LDS is released
 
   const float l_tot = xor32_sum(xor16_sum(l));
   if (l16 < G) {
@@ -431,7 +494,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
     const size_t pidx = ((size_t)b * a.Hq + hq) * a.n_split + split;
     float* po = a.part_o + pidx * D;
 #pragma unroll
-    for (int db = 0; db < D / 16; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
+    for (int db = 0; db < NB; db++) *(f32x4_t*)(po + 16 * db + 4 * g) = o[db];
     if (g == 0) {
       a.part_ml[2 * pidx] = m_ref;
       a.part_ml[2 * pidx + 1] = l_tot;
@@ -897,53 +960,29 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
 
 }  // namespace
 
-SplitPlan gqa_decode_plan(int B, int Hq, int max_len) {
-  (void)Hq;
-  int chunk = 1024;
-  // keep at least ~2048 waves for small batches
-  while (chunk > TK && (long)B * 8 * ((max_len + chunk - 1) / chunk) < 2048) chunk /= 2;
-  SplitPlan p;
-  p.chunk = chunk;
-  p.n_split = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
-  return p;
-}
-
-SplitPlan mla_decode_plan(int B, int H, int max_len) {
-  (void)H;
-  // one workgroup per CU: aim for >= 256 workgroups in total
-  int want = B > 0 ? (256 + B - 1) / B : 1;
-  int n_tiles = max_len > 0 ? (max_len + TK - 1) / TK : 1;
-  want = max(1, min(want, n_tiles));
-  int chunk = ((n_tiles + want - 1) / want) * TK;
-  SplitPlan p;
-  p.chunk = chunk;
-  p.n_split = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
-  return p;
-}
-
-size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split) {
-  const size_t rows = (size_t)B * Hq * n_split;
-  const size_t o_bytes = (rows * Dv * 4 + 255) / 256 * 256;
-  return o_bytes + rows * 2 * 4;
-}
-
-hipError_t launch_gqa_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
-  const int G = a.Hq / a.Hkv;
-  const int grid = a.n_split * ((a.B + 7) / 8 * 8) * a.Hkv;  // see gqa_item
-  switch (G) {
-#define FA_G(n)                                                   \
-  case n:                                                         \
-    if (fp8) gqa_decode_split_fp8<n><<<grid, 64, 0, s>>>(a);      \
-    else gqa_decode_split<n><<<grid, 64, 0, s>>>(a);              \
+template <int D>
+hipError_t launch_gqa_split(const DecodeArgs& a, bool fp8, int grid, hipStream_t s) {
+  switch (a.Hq / a.Hkv) {
+#define FA_G(n)                                                     \
+  case n:                                                           \
+    if (fp8) gqa_decode_split_fp8<D, n><<<grid, 64, 0, s>>>(a);     \
+    else gqa_decode_split<D, n><<<grid, 64, 0, s>>>(a);             \
     break;
     FA_G(1) FA_G(2) FA_G(3) FA_G(4) FA_G(5) FA_G(6) FA_G(7) FA_G(8)
     FA_G(9) FA_G(10) FA_G(11) FA_G(12) FA_G(13) FA_G(14) FA_G(15) FA_G(16)
 #undef FA_G
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_gqa_decode(const DecodeArgs& a, int D, bool fp8, hipStream_t s) {
+  const int grid = a.n_split * ((a.B + 7) / 8 * 8) * a.Hkv;  // see gqa_item
+  hipError_t e = D == 128 ? launch_gqa_split<128>(a, fp8, grid, s)
+               : D == 64  ? launch_gqa_split<64>(a, fp8, grid, s)
+                          : hipErrorInvalidValue;
   if (e != hipSuccess) return e;
-  combine_kernel<<<(a.B * a.Hq * (128 / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, 128);
+  combine_kernel<<<(a.B * a.Hq * (D / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, D);
   return hipGetLastError();
 }
 

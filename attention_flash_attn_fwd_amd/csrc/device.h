@@ -128,6 +128,43 @@ __device__ __forceinline__ void lds_b128_x8(i32x4_t (&r)[8], const uint32_t (&a)
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
+// Four and six 16-byte LDS reads as one self-waiting block (see lds_tr16_x8).
+__device__ __forceinline__ void lds_b128_x4(i32x4_t (&r)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
+__device__ __forceinline__ void lds_b128_x6(i32x4_t (&r)[6], const uint32_t (&a)[6]) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b128 %4, %10\n\t"
+      "ds_read_b128 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+// Four ds_read_b64_tr_b8 as one self-waiting block.
+__device__ __forceinline__ void lds_tr8_x4(i32x2_t (&r)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %4\n\t"
+      "ds_read_b64_tr_b8 %1, %5\n\t"
+      "ds_read_b64_tr_b8 %2, %6\n\t"
+      "ds_read_b64_tr_b8 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const FA_LDS char* p) { return (uint32_t)(uintptr_t)p; }
 
 __device__ __forceinline__ i32x4_t cat(i32x2_t a, i32x2_t b) {

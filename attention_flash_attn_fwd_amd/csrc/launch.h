@@ -7,6 +7,9 @@
 
 namespace fa {
 
+// Keys per K/V tile of the decode kernels (the split sizes of the decode plans are multiples).
+constexpr int kDecodeTileKeys = 32;
+
 struct PrefillArgs {
   const void* q;        // MHA: q; MLA: q_nope
   const void* k;        // MHA: k; MLA: k_nope
@@ -35,7 +38,7 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   const float* k_scale; // e4m3 caches: GQA [B, max_len, Hkv] per key row, MLA [B, max_len]; else NULL
   const float* v_scale; // e4m3 GQA cache: [B, max_len, Hkv]; else NULL
-  float* part_o;        // workspace: [B, Hq, n_split, Dv] fp32
+  float* part_o;        // workspace: [B, Hq, n_split, Dv] fp32 (GQA: Dv = D)
   float* part_ml;       // workspace: [B, Hq, n_split, 2] fp32 (row max, row sum)
   int B, Hq, Hkv, max_len;
   int n_split, chunk;   // keys per split
@@ -74,11 +77,11 @@ struct SplitPlan {
   int chunk;
   int n_split;
 };
-SplitPlan gqa_decode_plan(int B, int Hq, int max_len);
+SplitPlan gqa_decode_plan(int B, int Hkv, int max_len);
 SplitPlan mla_decode_plan(int B, int H, int max_len);
 size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split);
 
-hipError_t launch_gqa_decode(const DecodeArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_gqa_decode(const DecodeArgs& a, int D, bool fp8, hipStream_t s);
 hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s);
 
 }  // namespace fa

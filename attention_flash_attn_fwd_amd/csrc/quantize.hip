@@ -87,12 +87,6 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantArgs a) {
 
 }  // namespace
 
-int quantize_lanes_per_row(int cols) {
-  int lr = 1;
-  while (lr < 64 && 4 * lr < cols) lr <<= 1;
-  return lr;
-}
-
 hipError_t launch_quantize_rows(const QuantArgs& a, hipStream_t s) {
   const int Lr = a.lanes_per_row;
   int nk = (a.cols + 4 * Lr - 1) / (4 * Lr);

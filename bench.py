@@ -1,12 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the forward-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
 
 A step is one call of the path's entry point over the whole workload, inputs resident
-in HBM.  The default workload is the causal bf16 prefill (B4 H32 S4096 D128); the
-others (fp32 MHA, GQA decode, MLA decode, MLA prefill) can be named with --workload.
-Prints one JSON line with the throughput, a roofline object for the dominant kernel
+in HBM.  By default every workload is timed: the headline line is the causal bf16
+prefill (B4 H32 S4096 D128); the fp32 MHA, GQA decode, MLA decode and MLA prefill
+workloads and those of the next rows (e4m3 caches, e4m3 V, ragged prefill, merge,
+quantiser) follow in its "configs" array, each with its own roofline object
 (algorithmic work per launch / measured launch duration, against MI355X's published
 peak) and the CPU oracle timed on a bounded sample of the same workload.
 """
@@ -83,15 +84,25 @@ def algorithmic_work(w, lens=None):
     raise ValueError(w.kind)
 
 
+def _strip_comments(text: str) -> str:
+    """C/C++ source without // and /* */ comments and blank lines, each line right-stripped
+    (string literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def source_digest() -> str:
-    """sha256 over the kernel and ABI sources, to tie stored counter readings to a build."""
+    """sha256 over the kernel and ABI sources with comments removed, to tie stored counter
+    readings to the code they were taken on (a comment-only edit keeps the digest)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_flash_attn_fwd_amd", "csrc")
     for n in sorted(os.listdir(csrc)):
         if n.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, n), "rb") as f:
-                h.update(n.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, n), encoding="utf-8") as f:
+                h.update(n.encode() + b"\0" + _strip_comments(f.read()).encode())
     return h.hexdigest()
 
 
@@ -135,7 +146,7 @@ def setup(w):
     if w.kind == "decode":
         d = make_decode(w)
         q, kv_lens = bf16(d["q"]), torch.from_numpy(d["kv_lens"]).cuda()
-        ws = torch.empty(fa.decode_workspace_size(w.B, w.Hq, w.D, w.Skv), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(fa.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.Skv), dtype=torch.uint8, device="cuda")
         o = torch.empty_like(q)
         if w.dtype == "fp8":
             k, v, ks, vs = (torch.from_numpy(d[n]).cuda() for n in ("k", "v", "k_scale", "v_scale"))
@@ -333,36 +344,10 @@ def copy_calibration(steps: int):
 
 # ------------------------------------------------------------------------------- main
 
-def main():
-    from workloads.shapes import BENCH_DEFAULT, WORKLOADS
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--spinup", type=float, default=0.5,
-                    help="seconds of untimed steps before the warmup steps, so that GPU clocks settle")
-    ap.add_argument("--workload", default=BENCH_DEFAULT, choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work in the CPU sample")
-    ap.add_argument("--traffic", default=None, help="JSON with HBM traffic per launch from rocprofv3 counters (default profiles/traffic.json)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="time a plain 1 GiB device-to-device copy instead (scales FETCH_SIZE/WRITE_SIZE)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is a design note, "
-              "not built)", file=sys.stderr)
-        sys.exit(2)
-
+def timed(w, step, args):
+    """Untimed spin-up and warmup steps, then K timed steps; returns (ms per step by the host
+    clock, mean launch duration by HIP events on the launch stream, in ms)."""
     import torch
-    from workloads import workload
-    if args.copy_calibration:
-        copy_calibration(args.steps)
-        return
-    w = workload(args.workload)
-    torch.cuda.set_device(0)
-    step, lens, keep = setup(w)
-    flops, byts = algorithmic_work(w, lens)
-
     # clocks ramp up over the first tens of milliseconds of sustained load: run untimed steps
     # for a fixed time first, then the requested warmup steps
     t_spin = time.perf_counter()
@@ -373,18 +358,32 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record()
+        starts[i].record(stream)
         step(i)
-        ends[i].record()
+        ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    return wall * 1e3 / args.steps, sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+
+
+DTYPE_NAMES = {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16",
+               "fp8v": "e4m3 nope and V (bf16 P.V), bf16 rope", "fp8": "e4m3 cache, bf16 q/o"}
+
+
+def measure(w, args, cpu_budget, traffic_rec):
+    """One workload: device inputs, timed steps, roofline, oracle baseline.  Returns a dict."""
+    import torch
+    step, lens, keep = setup(w)
+    flops, byts = algorithmic_work(w, lens)
+    ms_per_step, launch_ms = timed(w, step, args)
+    del keep, step
+    torch.cuda.empty_cache()
 
     if w.kind in ("prefill", "prefill_varlen", "mla_prefill"):
         if w.kind == "mla_prefill":
@@ -400,22 +399,17 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "kernel": KERNELS[w.kind]}
         unit = "TFLOP/s"
-    else:  # decode and quantisation: HBM-bound
+    else:  # decode, merge and quantisation: HBM-bound
         value = byts / (ms_per_step * 1e-3) / 1e9
         achieved = byts / (launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK["hbm"], "unit": "GB/s",
                 "frac": round(achieved / PEAK["hbm"], 4), "kernel": KERNELS[w.kind]}
+        if w.kind in ("decode", "mla_decode"):
+            # decode sits near the ridge for MLA: report the matrix-core side too
+            fl = 2 * w.Hq * (w.D + w.Dv) * int(sum(lens))
+            roof["mfma_frac"] = round(fl / (launch_ms * 1e-3) / 1e12 / PEAK["bf16"], 4)
         unit = "GB/s"
-    traffic = None
-    tpath = args.traffic or os.path.join(ROOT, "profiles", "traffic.json")
-    if os.path.exists(tpath):
-        with open(tpath) as f:
-            tr = json.load(f)
-        rec = tr.get("workloads", {}).get(w.name)
-        # counters describe the kernels they were taken on: ignore them once the sources changed
-        if rec is not None and tr.get("source_sha256") == source_digest():
-            traffic = rec.get("bytes_per_launch")
-    roof["traffic"] = traffic
+    roof["traffic"] = None if traffic_rec is None else traffic_rec.get("bytes_per_launch")
 
     cfg = {"workload": w.name, "B": w.B, "Sq": w.Sq, "Skv": w.Skv, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
            "Dv": w.Dv, "causal": w.causal, "parallelism": "none (1 GPU)"}
@@ -427,17 +421,78 @@ def main():
     elif lens is not None:
         cfg.update({"sum_kv_len": int(sum(lens)), "len_range": [w.len_lo, w.len_hi]})
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "spinup_s": args.spinup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32->e4m3" if w.kind == "quantize" else "bf16 (fp32 LSE)" if w.kind == "merge" else {"f32": "f32", "bf16": "bf16", "fp8+bf16": "fp8e4m3+bf16", "fp8v": "e4m3 nope and V (bf16 P.V), bf16 rope",
-                                                           "fp8": "e4m3 cache, bf16 q/o"}[w.dtype],
-        "data": "synthetic (seeded N(0,1), see workloads/)", "config": cfg, "roofline": roof,
-        "kernel_ms": round(launch_ms, 4), "algorithmic": {"flops": flops if not isinstance(flops, tuple) else list(flops),
-                                                          "bytes": byts},
+        "value": round(value, 3), "unit": unit, "ms_per_step": round(ms_per_step, 4),
+        "dtype": "f32->e4m3" if w.kind == "quantize" else "bf16 (fp32 LSE)" if w.kind == "merge" else DTYPE_NAMES[w.dtype],
+        "config": cfg, "roofline": roof, "kernel_ms": round(launch_ms, 4),
+        "algorithmic": {"flops": flops if not isinstance(flops, tuple) else list(flops), "bytes": byts},
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_budget)
+    if cpu_budget > 0:
+        out["cpu_baseline"] = cpu_baseline(w, lens, cpu_budget)
+    return out
+
+
+def main():
+    from workloads.shapes import BENCH_DEFAULT, BENCH_ORDER, WORKLOADS
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spinup", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps, so that GPU clocks settle")
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS),
+                    help="one workload alone, or all of them (the headline first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of oracle work in the CPU sample of the headline workload")
+    ap.add_argument("--cpu-budget-other", type=float, default=2.0,
+                    help="seconds of oracle work in the CPU sample of each other workload")
+    ap.add_argument("--traffic", default=None, help="JSON with HBM traffic per launch from rocprofv3 counters (default profiles/traffic.json)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device-to-device copy instead (scales FETCH_SIZE/WRITE_SIZE)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (multi-GPU sharding is a design note, "
+              "not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import workload
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+    torch.cuda.set_device(0)
+
+    traffic = {}
+    tpath = args.traffic or os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        # counters describe the kernels they were taken on: ignore them once the code changed
+        if tr.get("source_sha256") == source_digest():
+            traffic = tr.get("workloads", {})
+
+    names = [args.workload] if args.workload != "all" else [BENCH_DEFAULT] + [n for n in BENCH_ORDER if n != BENCH_DEFAULT]
+    results = []
+    for i, name in enumerate(names):
+        w = workload(name)
+        budget = 0.0 if args.no_cpu_baseline else (args.cpu_budget if i == 0 else args.cpu_budget_other)
+        r = measure(w, args, budget, traffic.get(name))
+        results.append(r)
+        if len(names) > 1:
+            print(f"bench: {name}: {r['value']} {r['unit']} ({r['kernel_ms']} ms per launch, "
+                  f"{r['roofline']['frac']} of peak)", file=sys.stderr, flush=True)
+    head = results[0]
+    out = {
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "spinup_s": args.spinup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
+        "data": "synthetic (seeded N(0,1), see workloads/)", "config": head["config"], "roofline": head["roofline"],
+        "kernel_ms": head["kernel_ms"], "algorithmic": head["algorithmic"],
+    }
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if len(results) > 1:
+        out["configs"] = [dict(r, workload=r["config"]["workload"]) for r in results[1:]]
     print(json.dumps(out), flush=True)
 
 

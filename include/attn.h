@@ -128,10 +128,13 @@ int attn_merge_fwd(const void* o_a, const float* lse_a, const void* o_b, const f
  * The KV range of every sequence is split across workgroups; each writes a partial
  * (row max, row sum, unnormalised O) to `workspace`, and a second kernel on the same
  * stream merges the partials.  workspace: device memory of at least
- * attn_decode_workspace_size(B, Hq, D, max_kv_len) bytes, owned by the caller.
- *   Supported: dtype ATTN_BF16 or ATTN_FP8_E4M3, D == 128, Hq % Hkv == 0, Hq / Hkv <= 16.
+ * attn_decode_workspace_size(B, Hq, Hkv, D, max_kv_len) bytes, owned by the caller (the
+ * split count, and so the size, depends on the number of kv heads: one workgroup per
+ * (split, batch, kv head)).  The size query returns 0 for invalid sizes.
+ *   Supported: dtype ATTN_BF16 or ATTN_FP8_E4M3, D in {64, 128}, Hq % Hkv == 0,
+ *   Hq / Hkv <= 16.
  */
-size_t attn_decode_workspace_size(int B, int Hq, int D, int max_kv_len);
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len);
 int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o,
                     float* lse, const int32_t* kv_lens, const float* k_scale,
                     const float* v_scale, int dtype, int B, int Hq, int Hkv, int D,

@@ -26,7 +26,16 @@ def header_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    return fa.lib()
+    """libattn.so, or the library named by ATTN_ABI_TEST_LIB (the host-only sanitizer build of
+    the same C ABI, see tests/test_abi_sanitized.py)."""
+    path = os.environ.get("ATTN_ABI_TEST_LIB")
+    if not path:
+        return fa.lib()
+    l = ctypes.CDLL(path)
+    for name, (res, args) in fa.EXPORTS.items():
+        f = getattr(l, name)
+        f.restype, f.argtypes = res, args
+    return l
 
 
 def test_header_declares_the_four_entry_points():
@@ -43,9 +52,10 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
+    name = lambda code: lib.attn_status_string(code).decode()
     for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ESCALE):
-        assert fa.status_string(code) and fa.status_string(code) != "unknown status"
-    assert fa.status_string(12345) == "unknown status"
+        assert name(code) and name(code) != "unknown status"
+    assert name(12345) == "unknown status"
 
 
 def prefill(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, dtype=1, B=1, Sq=8, Skv=8, Hq=2, Hkv=1, D=128, causal=0, scale=0.1):
@@ -79,13 +89,15 @@ def decode(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, ks=NUL, vs=NUL, dtype
 
 
 def test_decode_validation(lib):
-    need = lib.attn_decode_workspace_size(4, 32, 128, 1024)
+    need = lib.attn_decode_workspace_size(4, 32, 8, 128, 1024)
     assert need > 0
-    assert lib.attn_decode_workspace_size(-1, 32, 128, 1024) == 0
+    assert lib.attn_decode_workspace_size(-1, 32, 8, 128, 1024) == 0
+    assert lib.attn_decode_workspace_size(4, 32, 0, 128, 1024) == 0
     assert decode(lib, dtype=0) == EDTYPE
     assert decode(lib, Hq=30, Hkv=8) == ESHAPE
     assert decode(lib, L=-1) == ESHAPE
-    assert decode(lib, D=64) == EUNSUP
+    assert decode(lib, D=96) == EUNSUP
+    assert decode(lib, D=256) == EUNSUP
     assert decode(lib, Hq=64, Hkv=2) == EUNSUP       # 32 q heads per kv head > 16
     assert decode(lib, scale=-1.0) == ESCALE
     assert decode(lib, lens=NUL) == ENULL
@@ -93,11 +105,27 @@ def test_decode_validation(lib):
     assert decode(lib, ws=NUL) == EWS
     assert decode(lib, wsb=need - 1) == EWS
     assert decode(lib, B=0, q=NUL, o=NUL, lens=NUL, ws=NUL) == OK
+    # head dim 64: the workspace of its own shape is enough, one byte less is not
+    need64 = lib.attn_decode_workspace_size(4, 32, 8, 64, 1024)
+    assert 0 < need64 < need
+    assert decode(lib, D=64, wsb=need64 - 1) == EWS
     # e4m3 caches carry per-token scales; bf16 caches take none
     assert decode(lib, dtype=2, ks=NUL, vs=FAKE) == ENULL
     assert decode(lib, dtype=2, ks=FAKE, vs=NUL) == ENULL
     assert decode(lib, dtype=1, ks=FAKE, vs=FAKE) == EDTYPE
-    assert decode(lib, dtype=2, ks=FAKE, vs=FAKE, D=64) == EUNSUP
+    assert decode(lib, dtype=2, ks=FAKE, vs=FAKE, D=96) == EUNSUP
+
+
+def test_decode_split_plan_follows_the_kv_heads(lib):
+    """One wave per (split, batch, kv head): fewer kv heads take more (shorter) splits, so the
+    workspace (one partial row per (batch, q head, split)) grows as Hkv shrinks, and a long
+    batch of many kv heads keeps its 1024-key splits."""
+    row = 128 * 4 + 2 * 4           # fp32 partial O row + (m, l) per (batch, q head, split)
+    ws = {hkv: lib.attn_decode_workspace_size(2, 16, hkv, 128, 65536) for hkv in (1, 2, 4, 8, 16)}
+    assert ws[1] > ws[2] > ws[4] > ws[8] > ws[16]
+    # B=64, Hkv=8, 8192 keys: 8 splits of 1024 keys give 4096 waves, no shortening needed
+    big = lib.attn_decode_workspace_size(64, 32, 8, 128, 8192)
+    assert abs(big - 64 * 32 * 8 * row) < 512
 
 
 def mla_prefill(lib, qn=FAKE, qr=FAKE, kn=FAKE, kr=FAKE, v=FAKE, o=FAKE, vs=NUL, dt=2, vdt=1, B=1, Sq=64, Skv=64,

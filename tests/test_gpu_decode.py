@@ -262,3 +262,150 @@ def test_mla_decode_fp8_matches_bf16_on_the_dequantised_cache():
     ob = fa.mla_decode(q, kvb, kl, dv=512, scale=w.scale)
     torch.cuda.synchronize()
     assert_close(host_f64(o8), host_f64(ob), BF16_TOL, "e4m3 vs bf16 path")
+
+
+# ------------------------------------------------------------------------------------------
+# Head dim 64 (bf16 and e4m3 caches)
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (16, 1), (12, 4), (14, 2)])
+def test_gqa_decode_d64(Hq, Hkv):
+    lens = [1, 31, 32, 33, 257, 1000, 0, 513]
+    w = workload(GQA, B=len(lens), Hq=Hq, Hkv=Hkv, Skv=1000, D=64, Dv=64, scale=64 ** -0.5)
+    _check_gqa(w, lens)
+    w8 = workload(GQA8, B=len(lens), Hq=Hq, Hkv=Hkv, Skv=1000, D=64, Dv=64, scale=64 ** -0.5)
+    say(f"case gqa decode e4m3 D=64 Hq={Hq} Hkv={Hkv} lens={lens}")
+    (q, k, v, kl, ks, vs), kd, vd = _gqa8(w8, lens=lens)
+    o, lse = fa.decode(q, k, v, kl, scale=w8.scale, return_lse=True, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(host_f64(q), kd, vd, np.asarray(lens), w8.scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O e4m3")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE e4m3")
+
+
+def test_gqa_decode_d64_long_sequences():
+    """Head dim 64 over a batch with long sequences (many 1024-key splits) and a single long one."""
+    lens = [8192, 5000, 1024, 3333]
+    _check_gqa(workload(GQA, B=4, Hq=32, Hkv=8, Skv=8192, D=64, Dv=64, scale=64 ** -0.5), lens)
+    _check_gqa(workload(GQA, B=1, Hq=4, Hkv=1, Skv=12000, D=64, Dv=64, scale=64 ** -0.5), [11999])
+
+
+# ------------------------------------------------------------------------------------------
+# Invariants of the split-KV path: the result does not depend on how the keys are split, and
+# a call repeated on the same inputs gives the same bits.
+
+def _pad_cache(x: torch.Tensor, L: int) -> torch.Tensor:
+    """The same cache rows in a cache of max length L (rows past the old end are zero)."""
+    out = torch.zeros((x.shape[0], L) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+    out[:, :x.shape[1]] = x
+    return out
+
+
+def test_gqa_decode_independent_of_the_split_plan():
+    """The same sequences in caches of max length 1024, 4096 and 16384: the split planner cuts
+    them into 32-, 128- and 512-key splits (one wave per (split, batch, kv head), at least
+    2048 waves); every result matches the oracle and the others."""
+    lens = [1000, 517, 33, 1, 999, 640, 256, 800]
+    for dtype_name in (GQA, GQA8):
+        w = workload(dtype_name, B=8, Hq=32, Hkv=8, Skv=1000)
+        outs = []
+        if dtype_name == GQA:
+            q, k, v, kl = _gqa(w, lens=lens)
+            kd, vd, extra = host_f64(k), host_f64(v), {}
+        else:
+            (q, k, v, kl, ks, vs), kd, vd = _gqa8(w, lens=lens)
+        ro, rl = oracle.decode(host_f64(q), kd, vd, np.asarray(lens), w.scale)
+        for L in (1024, 4096, 16384):
+            say(f"case gqa decode split plan {dtype_name} Lmax={L} ({fa.decode_workspace_size(8, 32, 8, 128, L)} B)")
+            if dtype_name == GQA:
+                o, lse = fa.decode(q, _pad_cache(k, L), _pad_cache(v, L), kl, scale=w.scale, return_lse=True)
+            else:
+                o, lse = fa.decode(q, _pad_cache(k, L), _pad_cache(v, L), kl, scale=w.scale, return_lse=True,
+                                   k_scale=_pad_cache(ks, L), v_scale=_pad_cache(vs, L))
+            torch.cuda.synchronize()
+            assert_close(host_f64(o), ro, BF16_TOL, f"O Lmax={L}")
+            assert_lse_close(lse.cpu().numpy(), rl, f"LSE Lmax={L}")
+            outs.append(host_f64(o))
+        for o in outs[1:]:
+            assert_close(o, outs[0], BF16_TOL, "against the 32-key splits")
+
+
+def test_mla_decode_independent_of_the_split_plan():
+    """MLA decode of the same sequences in latent caches of max length 1024, 8192 and 16384:
+    32-, 128- and 256-key splits."""
+    lens = [1000, 333, 1, 700]
+    for name in (MLA, MLA8):
+        w = workload(name, B=4, Hq=128, Skv=1000)
+        if name == MLA:
+            q, kv, kl = _mla(w, lens=lens)
+            kvd, extra = host_f64(kv), {}
+        else:
+            (q, kv, kl, ks), kvd = _mla8(w, lens=lens)
+        ro, rl = oracle.mla_decode(host_f64(q), kvd, np.asarray(lens), 512, w.scale)
+        outs = []
+        for L in (1024, 8192, 16384):
+            say(f"case mla decode split plan {name} Lmax={L} ({fa.mla_decode_workspace_size(4, 128, 512, L)} B)")
+            if name == MLA:
+                o, lse = fa.mla_decode(q, _pad_cache(kv, L), kl, dv=512, scale=w.scale, return_lse=True)
+            else:
+                o, lse = fa.mla_decode(q, _pad_cache(kv, L), kl, dv=512, scale=w.scale, return_lse=True,
+                                       kv_scale=_pad_cache(ks, L))
+            torch.cuda.synchronize()
+            assert_close(host_f64(o), ro, BF16_TOL, f"O Lmax={L}")
+            assert_lse_close(lse.cpu().numpy(), rl, f"LSE Lmax={L}")
+            outs.append(host_f64(o))
+        for o in outs[1:]:
+            assert_close(o, outs[0], BF16_TOL, "against the 32-key splits")
+
+
+def test_decode_calls_are_bitwise_repeatable():
+    """The same call twice gives identical bits (fixed merge order, no atomics), for GQA and MLA
+    decode with bf16 and e4m3 caches."""
+    lens = [1000, 517, 33, 1, 640]
+    w = workload(GQA, B=5, Hq=32, Hkv=8, Skv=1000)
+    q, k, v, kl = _gqa(w, lens=lens)
+    runs = [fa.decode(q, k, v, kl, scale=w.scale, return_lse=True) for _ in range(3)]
+    w8 = workload(GQA8, B=5, Hq=16, Hkv=2, Skv=1000, D=64, Dv=64, scale=64 ** -0.5)
+    (q8, k8, v8, kl8, ks, vs), _, _ = _gqa8(w8, lens=lens)
+    runs8 = [fa.decode(q8, k8, v8, kl8, scale=w8.scale, return_lse=True, k_scale=ks, v_scale=vs) for _ in range(3)]
+    wm = workload(MLA, B=5, Hq=128, Skv=1000)
+    qm, kvm, klm = _mla(wm, lens=lens)
+    runsm = [fa.mla_decode(qm, kvm, klm, dv=512, scale=wm.scale, return_lse=True) for _ in range(3)]
+    wm8 = workload(MLA8, B=5, Hq=64, Skv=1000)
+    (qm8, kvm8, klm8, ksm), _ = _mla8(wm8, lens=lens)
+    runsm8 = [fa.mla_decode(qm8, kvm8, klm8, dv=512, scale=wm8.scale, return_lse=True, kv_scale=ksm) for _ in range(3)]
+    torch.cuda.synchronize()
+    for name, rs in (("gqa bf16", runs), ("gqa e4m3 d64", runs8), ("mla bf16", runsm), ("mla e4m3", runsm8)):
+        say(f"case repeatability {name}")
+        for o, lse in rs[1:]:
+            assert torch.equal(o.view(torch.int16), rs[0][0].view(torch.int16)), name
+            assert torch.equal(lse.view(torch.int32), rs[0][1].view(torch.int32)), name
+
+
+def test_decode_identical_value_rows_return_that_row():
+    """If every visible V row is the same vector, the output is that vector whatever q and K are
+    (the softmax weights sum to one): GQA (bf16, e4m3) and MLA decode."""
+    lens = [700, 1, 64]
+    w = workload(GQA, B=3, Hq=8, Hkv=2, Skv=700)
+    q, k, v, kl = _gqa(w, lens=lens)
+    row = v[0, 0, :, :].clone()                           # [Hkv, D]
+    v[:] = row[None, None]
+    o = fa.decode(q, k, v, kl, scale=w.scale)
+    torch.cuda.synchronize()
+    ref = np.repeat(host_f64(row)[None], 3, axis=0).repeat(4, axis=1)   # head h reads kv head h // 4
+    assert_close(host_f64(o), ref, BF16_TOL, "GQA identical V rows")
+    w8 = workload(GQA8, B=3, Hq=8, Hkv=2, Skv=700)
+    (q8, k8, v8, kl8, ks, vs), _, _ = _gqa8(w8, lens=lens)
+    v8[:] = v8[0, 0][None, None]
+    vs[:] = vs[0, 0][None, None]
+    o8 = fa.decode(q8, k8, v8, kl8, scale=w8.scale, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    rowd = oracle.e4m3_to_f64(v8[0, 0].cpu().numpy()) * vs[0, 0].cpu().numpy()[:, None].astype(np.float64)
+    assert_close(host_f64(o8), np.repeat(rowd[None], 3, axis=0).repeat(4, axis=1), BF16_TOL, "GQA e4m3 identical V rows")
+    wm = workload(MLA, B=3, Hq=32, Skv=700)
+    qm, kvm, klm = _mla(wm, lens=lens)
+    # the first 512 columns (V) equal across rows; the rope columns (K only) stay random
+    kvm[:, :, :512] = kvm[0, 0, :512][None, None]
+    om = fa.mla_decode(qm, kvm, klm, dv=512, scale=wm.scale)
+    torch.cuda.synchronize()
+    refm = np.broadcast_to(host_f64(kvm[0, 0, :512]), (3, 32, 512))
+    assert_close(host_f64(om), refm, BF16_TOL, "MLA identical V rows")

@@ -7,7 +7,7 @@ import torch
 import attention_flash_attn_fwd_amd as fa
 import oracle
 from tests.helpers import (BF16_TOL, FP8_TOL, assert_close, assert_lse_close, dev, dev_bf16, host_f64, say)
-from workloads import make_mla_prefill, quantize_rows_e4m3, workload
+from workloads import e4m3_encode, make_mla_prefill, quantize_rows_e4m3, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +131,82 @@ def test_mla_prefill_fp8v_matches_bf16v_on_the_dequantised_values():
     ob, _ = _call(tb, w, True)
     torch.cuda.synchronize()
     assert_close(host_f64(o8), host_f64(ob), FP8_TOL, "e4m3 V vs bf16 V")
+
+
+# ------------------------------------------------------------------------------------------
+# Batches of several sequences with Sq != Skv: the per-batch offsets of q_nope, q_rope,
+# q_scale, k_nope, k_rope, k_scale, v and v_scale, and the bottom-right causal alignment.
+
+def _mla_general(B, Sq, Skv, H, Hr, nope_fp8, with_scales, v_fp8, seed):
+    """GPU tensors and the oracle's fp64 view of one MLA prefill problem."""
+    rng = np.random.default_rng(seed)
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    bf = lambda a: torch.from_numpy(a).cuda().to(torch.bfloat16)
+    qs = ks = None
+    if nope_fp8 and with_scales:
+        qc, qs = quantize_rows_e4m3(f(B, Sq, H, 128))
+        kc, ks = quantize_rows_e4m3(f(B, Skv, H, 128))
+    elif nope_fp8:
+        # raw e4m3 codes of small values (no scales: q_scale = k_scale = 1)
+        qc, kc = e4m3_encode(0.3 * f(B, Sq, H, 128)), e4m3_encode(0.3 * f(B, Skv, H, 128))
+    if nope_fp8:
+        qn_t, kn_t = dev(qc), dev(kc)
+        qn, kn = oracle.e4m3_to_f64(qc), oracle.e4m3_to_f64(kc)
+    else:
+        qn_t, kn_t = bf(f(B, Sq, H, 128)), bf(f(B, Skv, H, 128))
+        qn, kn = host_f64(qn_t), host_f64(kn_t)
+        if with_scales:
+            qs = rng.uniform(0.5, 2.0, (B, Sq, H)).astype(np.float32)
+            ks = rng.uniform(0.5, 2.0, (B, Skv, H)).astype(np.float32)
+    qr_t, kr_t = bf(f(B, Sq, H, 64)), bf(f(B, Skv, Hr, 64))
+    vs = None
+    if v_fp8:
+        vc, vs = quantize_rows_e4m3(f(B, Skv, H, 128))
+        v_t, v = dev(vc), oracle.e4m3_to_f64(vc) * vs[..., None].astype(np.float64)
+    else:
+        v_t = bf(f(B, Skv, H, 128))
+        v = host_f64(v_t)
+    t = dict(q_nope=qn_t, k_nope=kn_t, q_rope=qr_t, k_rope=kr_t, v=v_t,
+             q_scale=None if qs is None else dev(qs), k_scale=None if ks is None else dev(ks),
+             v_scale=None if vs is None else dev(vs))
+    x = dict(q_nope=qn, k_nope=kn, q_rope=host_f64(qr_t), k_rope=host_f64(kr_t), v=v,
+             q_scale=np.ones((B, Sq, H)) if qs is None else qs.astype(np.float64),
+             k_scale=np.ones((B, Skv, H)) if ks is None else ks.astype(np.float64))
+    return t, x
+
+
+MLA_BATCHED = [
+    # B, Sq, Skv, H, Hr, nope e4m3, scales, V e4m3, causal
+    (2, 77, 333, 3, 1, True, True, False, True),      # Sq < Skv, shared rope head
+    (3, 200, 90, 2, 2, True, True, False, True),      # Sq > Skv: leading rows see no key
+    (2, 150, 260, 2, 2, True, True, True, False),     # e4m3 V, one rope head per head
+    (3, 129, 65, 4, 1, True, True, True, True),       # e4m3 V, Sq > Skv
+    (2, 100, 300, 2, 1, False, True, False, True),    # bf16 nope with scales
+    (2, 190, 130, 3, 3, False, False, False, True),   # bf16 nope without scales, Sq > Skv
+    (3, 64, 200, 2, 2, False, True, True, False),     # bf16 nope, e4m3 V, non-causal
+    (2, 96, 257, 2, 1, True, False, False, True),     # e4m3 nope without scales
+    (2, 300, 300, 2, 1, True, True, False, True),     # Sq = Skv across two sequences
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,H,Hr,nope8,scales,v8,causal", MLA_BATCHED)
+def test_mla_prefill_batched(B, Sq, Skv, H, Hr, nope8, scales, v8, causal):
+    say(f"case mla prefill B={B} Sq={Sq} Skv={Skv} H={H} Hr={Hr} nope_e4m3={nope8} scales={scales} "
+        f"v_e4m3={v8} causal={causal}")
+    t, x = _mla_general(B, Sq, Skv, H, Hr, nope8, scales, v8, seed=100 + B * 7 + Sq)
+    o, lse = fa.mla_prefill(t["q_nope"], t["q_rope"], t["k_nope"], t["k_rope"], t["v"], t["q_scale"],
+                            t["k_scale"], causal=causal, scale=192 ** -0.5, return_lse=True, v_scale=t["v_scale"])
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_prefill(x["q_nope"], x["q_rope"], x["k_nope"], x["k_rope"], x["v"], x["q_scale"],
+                                x["k_scale"], 192 ** -0.5, causal)
+    tol = FP8_TOL if (nope8 or v8) else BF16_TOL
+    assert_close(host_f64(o), ro, tol, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
+    # each sequence alone gives the same rows (the batch offsets select the right sequence)
+    b = B - 1
+    ob = fa.mla_prefill(*(t[n][b:b + 1].contiguous() for n in ("q_nope", "q_rope", "k_nope", "k_rope", "v")),
+                        *(None if t[n] is None else t[n][b:b + 1].contiguous() for n in ("q_scale", "k_scale")),
+                        causal=causal, scale=192 ** -0.5,
+                        v_scale=None if t["v_scale"] is None else t["v_scale"][b:b + 1].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(ob[0].view(torch.int16), o[b].view(torch.int16)), "last sequence alone differs"

@@ -143,3 +143,23 @@ def test_binding_rejects_mismatched_outputs_and_workspaces():
     with pytest.raises(ValueError):
         fa.quantize_rows_e4m3(x, codes=torch.empty(4, 128, dtype=torch.uint8))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_first_causal_row_is_v0_and_identical_v_rows(D):
+    """Two invariants of the softmax: the first row of a causal prefill sees only key 0, so it
+    returns V[0]; and when every V row of a head is the same vector the output is that vector
+    (the weights sum to one), causal or not."""
+    w = workload("mha_prefill_causal_bf16_b4_h32_s4096_d128", B=2, Sq=300, Skv=300, Hq=4, Hkv=2, D=D, Dv=D,
+                 scale=D ** -0.5)
+    q, k, v = _inputs(w)
+    o = fa.prefill(q, k, v, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    v0 = host_f64(v[:, 0])                                   # [B, Hkv, D]
+    assert_close(host_f64(o[:, 0]), np.repeat(v0, 2, axis=1), BF16_TOL, "first causal row = V[0]")
+    v[:] = v[:, 7:8]
+    for causal in (True, False):
+        o = fa.prefill(q, k, v, causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        ref = np.broadcast_to(np.repeat(host_f64(v[:, 7:8]), 2, axis=2), o.shape)
+        assert_close(host_f64(o), ref, BF16_TOL, f"identical V rows causal={causal}")

@@ -96,8 +96,23 @@ WORKLOADS = {
         B=1, Hq=128, Hkv=128, Sq=8192, Skv=8192, D=128, Dv=128, Dn=128),
 }
 
-# The workload the benchmark times by default.
+# The headline workload of the benchmark.
 BENCH_DEFAULT = "mha_prefill_causal_bf16_b4_h32_s4096_d128"
+# Every workload the benchmark times by default, in order: the five workloads of the path,
+# then those of the next rows (e4m3 caches, e4m3 V, ragged prefill, merge, quantiser).
+BENCH_ORDER = [
+    "mha_prefill_causal_bf16_b4_h32_s4096_d128",
+    "mha_fp32_b1_h4_s128_d64",
+    "gqa_decode_bf16_b64_hq32_hkv8_d128_l8192",
+    "mla_decode_bf16_b64_h128_dk576_dv512_l4096",
+    "mla_prefill_fp8_causal_b1_h128_s8192",
+    "gqa_decode_fp8_b64_hq32_hkv8_d128_l8192",
+    "mla_decode_fp8_b64_h128_dk576_dv512_l4096",
+    "mla_prefill_fp8v_causal_b1_h128_s8192",
+    "mha_prefill_varlen_causal_bf16_b8_len512to3584_h32_d128",
+    "merge_bf16_b4_s4096_h32_d128",
+    "quantize_e4m3_rows_b1_s8192_h128_d128",
+]
 
 
 def workload(name: str, **overrides) -> Workload:
