@@ -42,13 +42,25 @@ __device__ __forceinline__ bool gqa_item(const DecodeArgs& a, int& kvh, int& spl
 // barriers: the wave is alone in its workgroup).  Every LDS read of a tile is an asm block
 // that waits for itself (lds_* in device.h), so no instruction the compiler sees consumes
 // a load result inside the loop: the only vector-memory waits are the explicit ones, and
-// GQA_NS - 1 tiles stay in flight while a tile is computed.  While fewer than GQA_NS - 1
-// tiles are left, each step issues the same number of copies into a spare LDS block that
-// is never read, at an offset past every buffer (they fetch nothing), so the wait count is
-// the same on every path and no copy is ever in flight into a stage being read.
-// Head dim D = 128 or 64.
+// GQA_NS - 1 tiles stay in flight while a tile is computed.  In the last GQA_NS - 1 steps
+// no tile is left to issue, and each waits for exactly the copies of the tiles still younger
+// than its own, so no copy is ever in flight into a stage being read.  Head dim D = 128 or 64.
 
 constexpr int GQA_NS = 4;  // LDS stages per wave
+
+// s_waitcnt vmcnt(younger * OPS): tile t has landed when at most the copies of the `younger`
+// tiles issued after it are still in flight (0 <= younger < GQA_NS; vector-memory loads
+// complete in order)
+template <int OPS>
+__device__ __forceinline__ void wait_tile(int younger) {
+  static_assert(GQA_NS == 4, "one case per count of younger tiles");
+  switch (younger) {
+    case 3: wait_vmcnt<3 * OPS>(); break;
+    case 2: wait_vmcnt<2 * OPS>(); break;
+    case 1: wait_vmcnt<OPS>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
 
 // 16-byte chunk swizzles of the GQA tiles not covered by device.h:
 //  * bf16 rows of 128 bytes (D = 64) alternate bank halves by parity.  With t = (row / 2) % 8,
@@ -81,9 +93,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
   constexpr int NC = D / 32;                        // S^T contraction steps
   constexpr int NB = D / 16;                        // 16-column blocks of O^T
   __shared__ __attribute__((aligned(1024))) char ring_raw[GQA_NS * STAGE];
-  __shared__ __attribute__((aligned(1024))) char spare_raw[1024];
   FA_LDS char* const ring = (FA_LDS char*)ring_raw;
-  FA_LDS char* const spare = (FA_LDS char*)spare_raw;
 
   int kvh, split, b;
   if (!gqa_item(a, kvh, split, b)) return;
@@ -161,29 +171,25 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
       }
     }
   };
-  auto issue_spare = [&]() {
-    const auto r = make_rsrc(kbase, ROWB);
-#pragma unroll
-    for (int i = 0; i < OPS; i++) dma16_buf(r, spare, kOutOfRange);
-  };
 
   float m_ref = -INFINITY, neg = 0.f, l = 0.f;
   f32x4_t o[NB];
 #pragma unroll
   for (int d = 0; d < NB; d++) o[d] = f32x4_t{};
 
-  // prologue: tiles 0 .. GQA_NS-2; then every step issues tile t + GQA_NS - 1 (or spare
-  // copies), so exactly GQA_NS - 1 tiles of copies are younger than tile t's
+  // prologue: tiles 0 .. GQA_NS-2; then every step issues tile t + GQA_NS - 1 while there is
+  // one, so min(GQA_NS - 1, n_tiles - 1 - t) tiles of copies are younger than tile t's
 #pragma unroll
-  for (int p = 0; p < GQA_NS - 1; p++) {
+  for (int p = 0; p < GQA_NS - 1; p++)
     if (p < n_tiles) issue(p);
-    else issue_spare();
-  }
   for (int t = 0; t < n_tiles; t++) {
     // the stage refilled here held tile t - 1, whose reads completed in their asm blocks
-    if (t + GQA_NS - 1 < n_tiles) issue(t + GQA_NS - 1);
-    else issue_spare();
-    wait_vmcnt<(GQA_NS - 1) * OPS>();
+    if (t + GQA_NS - 1 < n_tiles) {
+      issue(t + GQA_NS - 1);
+      wait_vmcnt<(GQA_NS - 1) * OPS>();
+    } else {
+      wait_tile<OPS>(n_tiles - 1 - t);
+    }
     asm volatile("" ::: "memory");
     const uint32_t st = lds_addr(ring) + (t % GQA_NS) * STAGE;
 
@@ -246,7 +252,6 @@ __global__ __launch_bounds__(64) void gqa_decode_split(DecodeArgs a) {
         o[4 * half + j] = mfma16x16x32_bf16(cat(vr[2 * j], vr[2 * j + 1]), pb, o[4 * half + j]);
     }
   }
-  wait_vmcnt<0>();  // the spare copies land before the LDS is released
 
   const float l_tot = xor32_sum(xor16_sum(l));
   if (l16 < G) {
@@ -295,9 +300,7 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
   constexpr int NC = D / 32;                        // S^T contraction steps
   constexpr int NB = D / 16;                        // 16-column blocks of O^T
   __shared__ __attribute__((aligned(1024))) char ring_raw[GQA_NS * STAGE];
-  __shared__ __attribute__((aligned(1024))) char spare_raw[1024];
   FA_LDS char* const ring = (FA_LDS char*)ring_raw;
-  FA_LDS char* const spare = (FA_LDS char*)spare_raw;
 
   int kvh, split, b;
   if (!gqa_item(a, kvh, split, b)) return;
@@ -386,27 +389,23 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
     dma4_buf(make_rsrc(ksbase + (size_t)key0 * a.Hkv, sbytes), dst + 2 * TILE, so);
     dma4_buf(make_rsrc(vsbase + (size_t)key0 * a.Hkv, sbytes), dst + 2 * TILE + SCB, so);
   };
-  auto issue_spare = [&]() {
-    const auto r = make_rsrc(kbase, ROWB);
-#pragma unroll
-    for (int i = 0; i < OPS; i++) dma16_buf(r, spare, kOutOfRange);
-  };
 
   float m_ref = -INFINITY, neg = 0.f, l = 0.f;
   f32x4_t o[NB];
 #pragma unroll
   for (int d = 0; d < NB; d++) o[d] = f32x4_t{};
 
-  // same ring discipline as the bf16 kernel: GQA_NS - 1 tiles of copies in flight
+  // same ring discipline as the bf16 kernel: up to GQA_NS - 1 tiles of copies in flight
 #pragma unroll
-  for (int p = 0; p < GQA_NS - 1; p++) {
+  for (int p = 0; p < GQA_NS - 1; p++)
     if (p < n_tiles) issue(p);
-    else issue_spare();
-  }
   for (int t = 0; t < n_tiles; t++) {
-    if (t + GQA_NS - 1 < n_tiles) issue(t + GQA_NS - 1);
-    else issue_spare();
-    wait_vmcnt<(GQA_NS - 1) * OPS>();
+    if (t + GQA_NS - 1 < n_tiles) {
+      issue(t + GQA_NS - 1);
+      wait_vmcnt<(GQA_NS - 1) * OPS>();
+    } else {
+      wait_tile<OPS>(n_tiles - 1 - t);
+    }
     asm volatile("" ::: "memory");
     const uint32_t st = lds_addr(ring) + (t % GQA_NS) * STAGE;
 
@@ -486,7 +485,6 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < NB; db++) o[db] = mfma16x16x32_bf16(e4m3x8_to_bf16(vr[db]), pb, o[db]);
   }
-  wait_vmcnt<0>();  // the spare copies land before the LDS is released
 
   const float l_tot = xor32_sum(xor16_sum(l));
   if (l16 < G) {

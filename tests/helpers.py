@@ -2,8 +2,8 @@
 the oracle, and the parity bars.
 
 Parity bars (max-abs error, relative L2 error over the compared tensor):
-  bf16 paths: 1e-2 and 5e-3; e4m3 nope path: 3e-2 and 1e-2 (against the oracle on the
-  dequantised inputs).  fp32 path: 1e-4 and 1e-5, derived from the arithmetic: fp32 products
+  bf16 paths: 1e-2 and 5e-3; e4m3 paths (MLA prefill nope or V, e4m3 decode caches): 3e-2 and
+  1e-2 (against the oracle on the dequantised inputs).  fp32 path: 1e-4 and 1e-5, derived from the arithmetic: fp32 products
   and sums over <= 4096 terms of O(1) values, exp2 to about 1 ulp, give errors of order 1e-6.
 """
 from __future__ import annotations
@@ -17,8 +17,17 @@ import oracle
 
 BF16_TOL = (1e-2, 5e-3)
 FP8_TOL = (3e-2, 1e-2)
+# Decode over e4m3 caches is an fp8 path: it is held to the fp8 bar against the oracle on the
+# dequantised cache.  The bf16 bar cannot hold there: a row with one visible key returns
+# bf16(v_scale) * code rounded to bf16 (P carries the value scale), two roundings of up to
+# 2^-9 relative each, i.e. up to 2^-8 |V|, past 1e-2 once |V| exceeds ~2.5.
+E4M3_CACHE_TOL = FP8_TOL
 F32_TOL = (1e-4, 1e-5)
-LSE_TOL = 2e-3
+# LSE (no bar is stated for it; derived from the arithmetic): the kernels sum the row's P after
+# rounding each value to bf16 (the P that multiplies V), so the row sum l carries a relative
+# error up to the bf16 unit roundoff 2^-8 when one key dominates, i.e. |d ln l| <= ln(1 + 2^-8)
+# = 3.9e-3, plus fp32 rounding of the scaled logits (< 5e-4 for |logit| < 10^3).
+LSE_TOL = 4.5e-3
 
 
 def say(msg: str):
