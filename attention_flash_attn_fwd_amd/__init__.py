@@ -28,6 +28,8 @@ EXPORTS = {
     "attn_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 5),
     "attn_decode_fwd": (ctypes.c_int, [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 +
                         [ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "attn_decode_fwd_static": (ctypes.c_int, [ctypes.c_void_p] * 8 + [ctypes.c_int] * 6 +
+                               [ctypes.c_float, ctypes.c_void_p]),
     "mla_prefill_fwd": (ctypes.c_int, [ctypes.c_void_p] * 10 + [ctypes.c_int] * 11 +
                         [ctypes.c_float, ctypes.c_void_p]),
     "mla_decode_workspace_size": (ctypes.c_size_t, [ctypes.c_int] * 4),
@@ -174,12 +176,7 @@ def decode_workspace_size(B: int, Hq: int, Hkv: int, D: int, max_kv_len: int) ->
     return int(lib().attn_decode_workspace_size(B, Hq, Hkv, D, max_kv_len))
 
 
-def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=None, out=None,
-           return_lse: bool = False, k_scale=None, v_scale=None):
-    """Decode: q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D], kv_lens int32 [B] (device) -> o [B,Hq,D] bf16.
-
-    Caches are bf16, or e4m3 codes (uint8 / float8_e4m3fn) with per-token fp32 scales
-    k_scale, v_scale [B,Lmax,Hkv]."""
+def _decode_operands(q, k_cache, v_cache, kv_lens, k_scale, v_scale):
     _need(q, "q", (torch.bfloat16,), 3); _need(kv_lens, "kv_lens", (torch.int32,), 1)
     fp8 = k_cache.dtype in _FP8
     if fp8:
@@ -195,6 +192,16 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=N
     Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
     if k_cache.shape[0] != B or k_cache.shape[3] != D or v_cache.shape != k_cache.shape or kv_lens.shape[0] != B:
         raise ValueError("shape mismatch")
+    return fp8, B, Hq, Hkv, D, Lmax
+
+
+def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=None, out=None,
+           return_lse: bool = False, k_scale=None, v_scale=None):
+    """Decode: q [B,Hq,D] bf16, caches [B,Lmax,Hkv,D], kv_lens int32 [B] (device) -> o [B,Hq,D] bf16.
+
+    Caches are bf16, or e4m3 codes (uint8 / float8_e4m3fn) with per-token fp32 scales
+    k_scale, v_scale [B,Lmax,Hkv]."""
+    fp8, B, Hq, Hkv, D, Lmax = _decode_operands(q, k_cache, v_cache, kv_lens, k_scale, v_scale)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     workspace, ws_bytes = _workspace(workspace, decode_workspace_size(B, Hq, Hkv, D, Lmax), q.device)
     o = torch.empty_like(q) if out is None else _out(out, "out", torch.bfloat16, q.shape, q.device)
@@ -204,6 +211,26 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float | None = None, workspace=N
                                B, Hq, Hkv, D, Lmax, scale, _ptr(workspace), ws_bytes, _stream())
     _check("attn_decode_fwd", st)
     return (o, lse) if return_lse else o
+
+
+DECODE_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_static(q, k_cache, v_cache, kv_lens, scale: float | None = None, out=None, lse=None,
+                  k_scale=None, v_scale=None):
+    """decode() without a workspace: the split partials live in the library's static per-GPU
+    buffer (attn_decode_fwd_static).  Pass `out` (and `lse`) to keep the call free of
+    allocations; calls that overlap in time on one GPU race for the buffer."""
+    fp8, B, Hq, Hkv, D, Lmax = _decode_operands(q, k_cache, v_cache, kv_lens, k_scale, v_scale)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else _out(out, "out", torch.bfloat16, q.shape, q.device)
+    if lse is not None:
+        _out(lse, "lse", torch.float32, (B, Hq), q.device)
+    st = lib().attn_decode_fwd_static(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(lse), _ptr(kv_lens),
+                                      _ptr(k_scale), _ptr(v_scale), ATTN_FP8_E4M3 if fp8 else ATTN_BF16,
+                                      B, Hq, Hkv, D, Lmax, scale, _stream())
+    _check("attn_decode_fwd_static", st)
+    return o
 
 
 def mla_prefill(q_nope, q_rope, k_nope, k_rope, v, q_scale=None, k_scale=None, causal: bool = True,

@@ -40,6 +40,7 @@ const char* attn_status_string(int status) {
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_HIP: return "HIP launch failed";
     case ATTN_ERR_SCALE: return "softmax_scale must be finite and positive";
+    case ATTN_ERR_SCRATCH: return "decode partials larger than the static scratch buffer";
     default: return "unknown status";
   }
 }
@@ -109,10 +110,14 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len)
   return fa::decode_workspace_bytes(B, Hq, D, p.n_split);
 }
 
-int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
-                    const int32_t* kv_lens, const float* k_scale, const float* v_scale, int dtype, int B,
-                    int Hq, int Hkv, int D, int max_kv_len, float softmax_scale, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Host validation of a GQA decode call and its launch arguments (all but the partials).
+int decode_args(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                const int32_t* kv_lens, const float* k_scale, const float* v_scale, int dtype, int B, int Hq,
+                int Hkv, int D, int max_kv_len, float softmax_scale, fa::DecodeArgs& a, size_t& need) {
   if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_DTYPE;
   const bool fp8 = dtype == ATTN_FP8_E4M3;
   if (!fp8 && (k_scale || v_scale)) return ATTN_ERR_DTYPE;  // scales belong to e4m3 caches only
@@ -126,17 +131,47 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
   const fa::SplitPlan p = fa::gqa_decode_plan(B, Hkv, max_kv_len);
   if (B > 65535 || p.n_split > 65535 || elems({p.n_split, Hkv, (B + 7) / 8 * 8}) > INT32_MAX) return ATTN_ERR_SHAPE;
   if (elems({B, Hq, D}) / 8 > INT32_MAX - 256) return ATTN_ERR_SHAPE;  // combine: one thread per 8 columns
-  const size_t need = fa::decode_workspace_bytes(B, Hq, D, p.n_split);
-  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  fa::DecodeArgs a{};
+  need = fa::decode_workspace_bytes(B, Hq, D, p.n_split);
+  a = fa::DecodeArgs{};
   a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = lse; a.kv_lens = kv_lens;
   a.k_scale = k_scale; a.v_scale = v_scale;
-  a.part_o = (float*)workspace;
-  a.part_ml = (float*)((char*)workspace + ((size_t)B * Hq * p.n_split * D * 4 + 255) / 256 * 256);
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.max_len = max_kv_len;
   a.n_split = p.n_split; a.chunk = p.chunk;
   a.scale = softmax_scale;
-  return hip_status(fa::launch_gqa_decode(a, D, fp8, stream));
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                    const int32_t* kv_lens, const float* k_scale, const float* v_scale, int dtype, int B,
+                    int Hq, int Hkv, int D, int max_kv_len, float softmax_scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  fa::DecodeArgs a;
+  size_t need = 0;
+  const int st = decode_args(q, k_cache, v_cache, o, lse, kv_lens, k_scale, v_scale, dtype, B, Hq, Hkv, D,
+                             max_kv_len, softmax_scale, a, need);
+  if (st != ATTN_OK || B == 0) return st;
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + ((size_t)B * Hq * a.n_split * D * 4 + 255) / 256 * 256);
+  return hip_status(fa::launch_gqa_decode(a, D, dtype == ATTN_FP8_E4M3, stream));
+}
+
+static_assert(ATTN_DECODE_STATIC_SCRATCH_BYTES == fa::kDecodeStaticScratchBytes, "static scratch size");
+
+int attn_decode_fwd_static(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                           const int32_t* kv_lens, const float* k_scale, const float* v_scale, int dtype, int B,
+                           int Hq, int Hkv, int D, int max_kv_len, float softmax_scale, hipStream_t stream) {
+  fa::DecodeArgs a;
+  size_t need = 0;
+  const int st = decode_args(q, k_cache, v_cache, o, lse, kv_lens, k_scale, v_scale, dtype, B, Hq, Hkv, D,
+                             max_kv_len, softmax_scale, a, need);
+  if (st != ATTN_OK || B == 0) return st;
+  if (need > fa::kDecodeStaticScratchBytes) return ATTN_ERR_SCRATCH;
+  return hip_status(fa::launch_gqa_decode_static(a, D, dtype == ATTN_FP8_E4M3, stream));
 }
 
 int mla_prefill_fwd(const void* q_nope, const void* q_rope, const void* k_nope, const void* k_rope, const void* v,

@@ -10,6 +10,7 @@
 // Both products use v_mfma_f32_16x16x32_bf16 in transposed form (S^T = K.Q^T and
 // O^T = V^T.P^T); the 16 MFMA columns hold query heads (the Hq/Hkv heads of a GQA group,
 // or 16 of the MLA heads).
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -982,6 +983,55 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, int D, bool fp8, hipStream_t s
   if (e != hipSuccess) return e;
   combine_kernel<<<(a.B * a.Hq * (D / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, D);
   return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// The split partials of attn_decode_fwd_static, for callers that cannot allocate device memory:
+// a buffer of fixed size in the code object, one copy per GPU, held until the process ends.
+// Every call on a GPU shares its copy, and nothing in it needs clearing between calls: the
+// combine reads only the partials of splits that start before their sequence's length, and
+// each of those splits writes its partial first.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a stand-in, not a device address): it passes the address
+// hipGetSymbolAddress returns for the device the stream runs on.
+static __device__ __align__(256) unsigned char scratch[kDecodeStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each device, once resolved
+}  // namespace
+
+// Device address of the static partials buffer on the device that stream s runs on (the
+// current device for the null stream), resolved once per device with that device current.
+static hipError_t static_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (e2 != hipSuccess) return e2;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_gqa_decode_static(DecodeArgs a, int D, bool fp8, hipStream_t s) {
+  void* p = nullptr;
+  const hipError_t e = static_scratch(s, &p);
+  if (e != hipSuccess) return e;
+  a.part_o = (float*)p;
+  a.part_ml = (float*)((char*)p + ((size_t)a.B * a.Hq * a.n_split * D * 4 + 255) / 256 * 256);
+  return launch_gqa_decode(a, D, fp8, s);
 }
 
 hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {

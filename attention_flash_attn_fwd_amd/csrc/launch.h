@@ -9,6 +9,8 @@ namespace fa {
 
 // Keys per K/V tile of the decode kernels (the split sizes of the decode plans are multiples).
 constexpr int kDecodeTileKeys = 32;
+// Size of the static split-partials buffer of attn_decode_fwd_static (per GPU).
+constexpr size_t kDecodeStaticScratchBytes = size_t(16) << 20;
 
 struct PrefillArgs {
   const void* q;        // MHA: q; MLA: q_nope
@@ -82,6 +84,9 @@ SplitPlan mla_decode_plan(int B, int H, int max_len);
 size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split);
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int D, bool fp8, hipStream_t s);
+// The same with the partials in the library's static per-GPU buffer (a.part_o / a.part_ml are
+// set here); the caller has checked that they fit in kDecodeStaticScratchBytes.
+hipError_t launch_gqa_decode_static(DecodeArgs a, int D, bool fp8, hipStream_t s);
 hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s);
 
 }  // namespace fa

@@ -57,7 +57,8 @@ typedef enum {
   ATTN_ERR_UNSUPPORTED = -4,  /* head dims / options outside the compiled set */
   ATTN_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than *_workspace_size() */
   ATTN_ERR_HIP = -6,          /* a HIP launch failed */
-  ATTN_ERR_SCALE = -7         /* softmax_scale not finite and positive */
+  ATTN_ERR_SCALE = -7,        /* softmax_scale not finite and positive */
+  ATTN_ERR_SCRATCH = -8       /* attn_decode_fwd_static: partials larger than its static buffer */
 } attn_status_t;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -140,6 +141,25 @@ int attn_decode_fwd(const void* q, const void* k_cache, const void* v_cache, voi
                     const float* v_scale, int dtype, int B, int Hq, int Hkv, int D,
                     int max_kv_len, float softmax_scale, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_decode_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace argument; the
+ * split partials go to a static buffer of ATTN_DECODE_STATIC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends.  The caller still passes q, the
+ * caches, kv_lens and o (and lse), exactly as for attn_decode_fwd, with the same results.
+ * The call allocates nothing.  It returns ATTN_ERR_SCRATCH, with nothing enqueued, when
+ * attn_decode_workspace_size(B, Hq, Hkv, D, max_kv_len) exceeds the buffer (for example B 64,
+ * Hq 32, Hkv 8, D 128 and 8192 keys need 8.5 MB).  All calls on one GPU share its buffer: calls
+ * that overlap in time there (on different streams without ordering) race and give undefined
+ * results; order them (one stream, or events).  The first call on a GPU resolves the buffer's
+ * address there (hipGetSymbolAddress); a failure of that returns ATTN_ERR_HIP.
+ */
+#define ATTN_DECODE_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_decode_fwd_static(const void* q, const void* k_cache, const void* v_cache, void* o,
+                           float* lse, const int32_t* kv_lens, const float* k_scale,
+                           const float* v_scale, int dtype, int B, int Hq, int Hkv, int D,
+                           int max_kv_len, float softmax_scale, hipStream_t stream);
 
 /*
  * MLA prefill with per-token scales (MLASmemStorage page: Q and KV tiles each hold a

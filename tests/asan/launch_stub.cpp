@@ -12,6 +12,7 @@ hipError_t launch_mla_prefill(const PrefillArgs&, bool, bool, hipStream_t) { ret
 hipError_t launch_merge(const MergeArgs&, bool, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_quantize_rows(const QuantArgs&, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_gqa_decode(const DecodeArgs&, int, bool, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_gqa_decode_static(DecodeArgs, int, bool, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_mla_decode(const DecodeArgs&, bool, hipStream_t) { return hipErrorInvalidValue; }
 
 }  // namespace fa

@@ -12,7 +12,7 @@ import attention_flash_attn_fwd_amd as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
 
-OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ESCALE = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ESCALE, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
 NUL = None
 S = ctypes.c_void_p(0)
@@ -53,7 +53,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_status_strings(lib):
     name = lambda code: lib.attn_status_string(code).decode()
-    for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ESCALE):
+    for code in (OK, ENULL, ESHAPE, EDTYPE, EUNSUP, EWS, EHIP, ESCALE, ESCRATCH):
         assert name(code) and name(code) != "unknown status"
     assert name(12345) == "unknown status"
 
@@ -126,6 +126,29 @@ def test_decode_split_plan_follows_the_kv_heads(lib):
     # B=64, Hkv=8, 8192 keys: 8 splits of 1024 keys give 4096 waves, no shortening needed
     big = lib.attn_decode_workspace_size(64, 32, 8, 128, 8192)
     assert abs(big - 64 * 32 * 8 * row) < 512
+
+
+def decode_static(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lens=FAKE, ks=NUL, vs=NUL, dtype=1, B=4, Hq=32, Hkv=8, D=128,
+                  L=1024, scale=0.1):
+    return lib.attn_decode_fwd_static(q, k, v, o, NUL, lens, ks, vs, dtype, B, Hq, Hkv, D, L, scale, S)
+
+
+def test_decode_static_validation(lib):
+    """The entry point without a workspace validates like attn_decode_fwd and rejects, before any
+    HIP call, partials larger than its static buffer (16 MiB)."""
+    assert decode_static(lib, dtype=0) == EDTYPE
+    assert decode_static(lib, Hq=30, Hkv=8) == ESHAPE
+    assert decode_static(lib, D=96) == EUNSUP
+    assert decode_static(lib, scale=0.0) == ESCALE
+    assert decode_static(lib, lens=NUL) == ENULL
+    assert decode_static(lib, dtype=2, ks=FAKE, vs=NUL) == ENULL
+    assert decode_static(lib, B=0, q=NUL, o=NUL, lens=NUL) == OK
+    limit = 16 << 20
+    # B 64, 32/8 heads, D 128, 8192 keys: 8.5 MB of partials fit; 16384 keys (17 MB) do not
+    assert lib.attn_decode_workspace_size(64, 32, 8, 128, 8192) <= limit
+    assert lib.attn_decode_workspace_size(64, 32, 8, 128, 16384) > limit
+    assert decode_static(lib, B=64, L=16384) == ESCRATCH
+    assert decode_static(lib, B=512, Hq=64, Hkv=8, L=8192) == ESCRATCH
 
 
 def mla_prefill(lib, qn=FAKE, qr=FAKE, kn=FAKE, kr=FAKE, v=FAKE, o=FAKE, vs=NUL, dt=2, vdt=1, B=1, Sq=64, Skv=64,
