@@ -229,16 +229,17 @@ struct QkMla {
 #pragma unroll
       for (int c = 0; c < 8; c++) sn = mfma32x32x16_bf16(lds_b128(stage + s.na[c] + kb * 32 * NROWB), q.n16[c], sn);
     }
-    f32x16_t sr{};
-#pragma unroll
-    for (int c = 0; c < 4; c++) sr = mfma32x32x16_bf16(lds_b128(stage + s.ra[c] + kb * 32 * 128), q.r[c], sr);
-    // this lane holds keys 32kb + 8j + 4hl + i in register 4j + i
+    // the nope product scaled by q_scale * k_scale in place, then the rope products accumulate
+    // onto it (one accumulator); this lane holds keys 32kb + 8j + 4hl + i in register 4j + i
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const f32x4_t ks = has_kscale ? lds_f32x4(stage + s.sa + (32 * kb + 8 * j) * 4) : f32x4_t{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-      for (int i = 0; i < 4; i++) acc[4 * j + i] = fmaf(sn[4 * j + i], q.qs * ks[i], sr[4 * j + i]);
+      for (int i = 0; i < 4; i++) sn[4 * j + i] *= q.qs * ks[i];
     }
+#pragma unroll
+    for (int c = 0; c < 4; c++) sn = mfma32x32x16_bf16(lds_b128(stage + s.ra[c] + kb * 32 * 128), q.r[c], sn);
+    acc = sn;
   }
 };
 
