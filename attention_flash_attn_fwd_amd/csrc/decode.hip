@@ -510,21 +510,35 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
 // O^T = V^T.P^T the pair splits the 512 output columns (hh selects 256 of them).  So a
 // wave keeps half of Q^T (72 VGPRs) and half of O^T (128), and every 16-byte K read or
 // 8-byte transposed V read feeds a 32x32 product.  The 576-wide latent tile (32 keys) is
-// copied once per workgroup into a three-stage LDS ring by direct loads; its first 512
+// copied once per workgroup into a two-stage LDS ring by direct loads; its first 512
 // columns are V, so the cache is read from HBM once.
 //
-// In LDS a latent row occupies 1280 bytes (1152 used), so every row starts on the same
-// bank; swz256 permutes the 16-byte chunks within each 256-byte group.
+// LDS tile layout ("chunk-column major"): 16-byte chunk c (8 latent columns) of key row r
+// sits at (c / 2) * 1024 + (c % 2) * 512 + ((r + 4 (c % 4)) % 32) * 16, i.e. each 1 KiB block
+// holds two chunk columns of all 32 rows, each column rotated by 4 (c % 4) row slots.  Then a
+// direct copy instruction moves one whole block (lane l: row slot l % 32 of column 2j + l / 32,
+// a source offset of one of two per-lane patterns plus 32 j), the K read of a contraction step
+// is one contiguous 1 KiB block, and the transposing V reads of a pass hit 16 distinct 16-byte
+// slots (all 64 banks once): no padding, and a handful of address registers.
 
 constexpr int MLA_DK = 576, MLA_DV = 512, MLA_ROWB = 1152, MLA_LROWB = 1280;
-constexpr int MLA_LTILE = TK * MLA_LROWB;             // 40 KiB per stage
-constexpr int MLA_NW = 8, MLA_NS = 3;
-constexpr int MLA_OPS = MLA_LTILE / 1024 / MLA_NW;    // direct copies per wave per tile
+constexpr int MLA_CTILE = TK * MLA_ROWB;              // 36 KiB per stage (bf16 kernel)
+constexpr int MLA_CBLK = MLA_CTILE / 1024;            // 36 one-KiB copy blocks per tile
+constexpr int MLA_LTILE = TK * MLA_LROWB;             // 40 KiB (row-padded tiles of the e4m3 kernel's scale path)
+constexpr int MLA_NW = 8, MLA_NS = 2;
+constexpr int MLA_OPS = MLA_LTILE / 1024 / MLA_NW;    // direct copies per wave per tile (e4m3 kernel)
 constexpr int MLA_KS = MLA_DK / 32;                   // contraction steps per wave (18)
 constexpr int MLA_DB = MLA_DV / 64;                   // 32-column output blocks per wave (8)
+constexpr int MLA_BW = 4;                             // waves of the bf16 kernel (one per SIMD)
+constexpr int MLA_QS = MLA_DK / 16;                   // its S contraction steps per wave (36)
+constexpr int MLA_OB = MLA_DV / 32 / MLA_BW;          // its 32-column output blocks per wave (4)
+static_assert(MLA_CBLK % MLA_BW == 0 && MLA_BW % 2 == 0, "bf16 tile copy split");
+constexpr int MLA_CPW = MLA_CBLK / MLA_BW;            // its direct copies per wave per tile (9)
+static_assert(MLA_CPW == MLA_QS / 4, "one copy per group of four S steps");
+constexpr float kMlaGrow = 64.f;                      // log2 bound of P against the fixed reference
 static_assert(MLA_LTILE % (1024 * MLA_NW) == 0, "tile copy split");
 
-// physical 16-byte chunk of logical chunk lc in LDS row `row`
+// physical 16-byte chunk of logical chunk lc in LDS row `row` (row-padded layout)
 __device__ __forceinline__ uint32_t mla_chunk(uint32_t row, uint32_t lc) {
   return (lc & ~15u) | ((lc & 15u) ^ swz256(row));
 }
@@ -541,12 +555,15 @@ __device__ __forceinline__ bool mla_item(const DecodeArgs& a, int& split, int& b
   return b < a.B;
 }
 
-__global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char st0_raw[MLA_LTILE];
-  __shared__ __attribute__((aligned(1024))) char st1_raw[MLA_LTILE];
-  __shared__ __attribute__((aligned(1024))) char st2_raw[MLA_LTILE];
-  __shared__ __attribute__((aligned(1024))) char xs_raw[MLA_NW * 4096];  // partial S^T per wave
-  FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw};
+__global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char ring_raw[3 * MLA_CTILE];
+  __shared__ __attribute__((aligned(1024))) char pt_raw[2 * MLA_BW * 2 * 1024];  // P^T of two tiles
+  // head group whose scores outgrew the reference, per tile parity; lanes other than 0 of a
+  // wave write their copy of the flag into a slot of their own (no branch on the lane), so
+  // that the flags of the four waves sit side by side in slot 0
+  __shared__ __attribute__((aligned(16))) int grow_s[2][64][MLA_BW];
+  FA_LDS char* const ring = (FA_LDS char*)ring_raw;
+  FA_LDS char* const pt = (FA_LDS char*)pt_raw;
 
   int split, b;
   if (!mla_item(a, split, b)) return;  // uniform over the workgroup
@@ -557,156 +574,214 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split(DecodeArgs a) {
   const int n_tiles = (end - start + TK - 1) / TK;
 
   const int wave = wave_id(), lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
-  const int hh = wave >> 2;
-  const int h = 32 * (wave & 3) + l32;
+  const int h = 32 * wave + l32;  // head of this lane in the S^T / softmax role
   const bool hvalid = h < a.Hq;
   const float c = a.scale * kLog2e;
 
-  // Q^T half as the B operand: column l32 = head h; step i covers latent columns
-  // 16 (2i + hh) + 8hl .. +7
-  i32x4_t qf[MLA_KS];
+  // Q^T of head group `wave` over the whole latent depth, as the B operand: column l32 = head
+  // h; step i covers latent columns 16i + 8hl .. +7
+  i32x4_t qf[MLA_QS];
   {
-    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * MLA_ROWB + 32 * hh + 16 * hl;
+    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * MLA_ROWB + 16 * hl;
 #pragma unroll
-    for (int i = 0; i < MLA_KS; i++) qf[i] = *(const i32x4_t*)(qp + 64 * i);
+    for (int i = 0; i < MLA_QS; i++) qf[i] = *(const i32x4_t*)(qp + 32 * i);
   }
   const char* kv = (const char*)a.k + (size_t)b * a.max_len * MLA_ROWB;
-  // direct copy of a tile: LDS byte o = blk*1024 + 16*lane is row o / 1280, physical chunk
-  // (o % 1280) / 16; it receives the logical chunk that maps there (padding slots are never
-  // read: their copies take an offset past the buffer's end, which fetches nothing)
-  auto issue = [&](int t, FA_LDS char* dst) {
-    const int key0 = start + t * TK, valid = min(TK, end - key0);
-    const auto r = make_rsrc(kv + (size_t)key0 * MLA_ROWB, (uint32_t)valid * MLA_ROWB);
-#pragma unroll
-    for (int i = 0; i < MLA_OPS; i++) {
-      const uint32_t blk = i * MLA_NW + wave, o = blk * 1024 + lane * 16;
-      const uint32_t row = o / MLA_LROWB, pc = (o % MLA_LROWB) >> 4;
-      const uint32_t lc = mla_chunk(row, pc);
-      const uint32_t rc = min(row, (uint32_t)(valid - 1));  // rows past the sequence repeat its last row
-      dma16_buf(r, dst + blk * 1024, lc < MLA_ROWB / 16 ? rc * MLA_ROWB + lc * 16 : kOutOfRange);
-    }
+  // direct copy k (0 .. 8) of a tile: block j = 4k + wave; lane l fills row slot l % 32 of
+  // chunk column 2j + l / 32, i.e. key row (l % 32 - 8 (j % 2) - 4 (l / 32)) mod 32.  Rows past
+  // the sequence repeat its last row; past the last tile the copies fetch nothing (an offset
+  // beyond the range).
+  const uint32_t crow = (uint32_t)(l32 - 8 * (wave & 1) - 4 * hl) & 31u;
+  const uint32_t ring_lds = lds_addr(ring) + wave * 1024;
+  struct Copy { i32x4_t r; uint32_t src, dst; };
+  auto plan_copy = [&](int t, int stage) {
+    const int tt = min(t, n_tiles - 1);
+    const int key0 = start + tt * TK, valid = min(TK, end - key0);
+    Copy cp;
+    cp.r = rsrc_words(kv + (size_t)key0 * MLA_ROWB, (uint32_t)valid * MLA_ROWB);
+    cp.src = t < n_tiles ? min(crow, (uint32_t)(valid - 1)) * MLA_ROWB + 16u * hl + 32u * wave : kOutOfRange;
+    cp.dst = ring_lds + stage * MLA_CTILE;
+    return cp;
   };
-  // S^T A operand: key row l32, logical chunk 2(2i + hh) + hl = 4i + 2hh + hl; its XOR part
-  // depends on i % 4 only
-  uint32_t koff[4];
-  {
-    const uint32_t sw = swz256(l32) ^ (2u * hh);
-#pragma unroll
-    for (int q = 0; q < 4; q++) koff[q] = l32 * MLA_LROWB + ((((4u * q + hl) & 15u) ^ sw) << 4);
-  }
-  // V^T reads (A operand of O^T): key rows 16tp + 8u + 4(g/2) + i16/4, output columns
-  // 256hh + 32db + 16(g%2) + 4(i16%4) .. +3; the XOR part depends on u and db % 4
-  uint32_t voff[2][4];
+  auto copy = [&](const Copy& cp, int k) { dma16_asm(cp.r, cp.dst + k * MLA_BW * 1024, cp.src + 32u * MLA_BW * k); };
+  // S^T A operand of step i: key row l32, chunk 2i + hl, at koff[i % 2] + 1024 i
+  const uint32_t koff0 = hl * 512 + ((l32 + 4 * hl) & 31) * 16;
+  const uint32_t koff1 = hl * 512 + ((l32 + 8 + 4 * hl) & 31) * 16;
+  // V^T reads (A operand of O^T) of P^T block tp, half u, output block d of this wave: key
+  // rows 16tp + 8u + 4(g/2) + i16/4, output columns 128 wave + 32d + 16(g%2) + 4(i16%4) .. +3
+  // (chunk 16 wave + 4d + 2(g%2) + (i16%4)/2), at voff[tp][u] + 2048 d
+  uint32_t voff[2][2];
   {
     const uint32_t g = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int u = 0; u < 2; u++)
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const uint32_t row = 8 * u + 4 * (g >> 1) + (i16 >> 2);
-        const uint32_t lc = 4 * q + 2 * (g & 1) + ((i16 & 3) >> 1);
-        voff[u][q] = row * MLA_LROWB + 512u * hh + ((lc ^ swz256(row)) << 4) + ((i16 & 1) << 3);
-      }
-  }
-
-  float m_ref = -INFINITY, neg = 0.f, l = 0.f;
-  f32x16_t o[MLA_DB];
-#pragma unroll
-  for (int d = 0; d < MLA_DB; d++) o[d] = f32x16_t{};
-  FA_LDS char* const xs_own = (FA_LDS char*)xs_raw + wave * 4096 + lane * 16;
-  const FA_LDS char* const xs_peer = (FA_LDS char*)xs_raw + (wave ^ 4) * 4096 + lane * 16;
-
-  auto tile = [&](auto SLOT, int t) {
-    constexpr int sl = decltype(SLOT)::value;
-    // tile t landed (the copies of tile t+1 may still be in flight), and every wave is
-    // done with tile t-1, whose stage is refilled with tile t+2 below
-    if (t + 1 < n_tiles) wait_vmcnt<MLA_OPS>();
-    else wait_vmcnt<0>();
-    barrier();
-    if (t + 2 < n_tiles) issue(t + 2, st[(sl + 2) % MLA_NS]);
-    const FA_LDS char* kt = st[sl];
-    // partial S^T over this wave's half of the contraction
-    f32x16_t s{};
-#pragma unroll
-    for (int i = 0; i < MLA_KS; i++) {
-      s = mfma32x32x16_bf16(lds_b128(kt + koff[i & 3] + 256 * (i >> 2)), qf[i], s);
-      if (i % 3 == 2) __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) *(FA_LDS f32x4_t*)(xs_own + 1024 * j) = f32x4_t{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
-    barrier();
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const f32x4_t pv = lds_f32x4(xs_peer + 1024 * j);
-#pragma unroll
-      for (int v = 0; v < 4; v++) s[4 * j + v] += pv[v];
-    }
-    // register v holds key 8(v/4) + 4hl + v%4 of the tile
-    const int key0 = start + t * TK;
-    if (key0 + TK > end) {
-      const int lim = end - key0 - 4 * hl;
-#pragma unroll
-      for (int v = 0; v < 16; v++) s[v] = (8 * (v >> 2) + (v & 3)) < lim ? s[v] : -INFINITY;
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int v = 1; v < 16; v++) mx = fmaxf(mx, s[v]);
-    mx = xor32_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx * c > m_ref * c + 8.f)) {  // lazy rescale (P <= 2^8)
-      const float m_new = fmaxf(m_ref, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast((m_ref - m_use) * c);
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < MLA_DB; d++) o[d] *= alpha;
-      m_ref = m_new;
-      neg = -m_use * c;
-    }
-    i32x4_t pb[2];
-#pragma unroll
-    for (int tp = 0; tp < 2; tp++) {
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) e[i] = exp2_fast(fmaf(s[8 * tp + i], c, neg));
-      pb[tp] = i32x4_t{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]), pack_bf16(e[4], e[5]), pack_bf16(e[6], e[7])};
-#pragma unroll
-      for (int i = 0; i < 4; i++) l = dot2_bf16(pb[tp][i], kBf16PairOne, l);
-    }
+    const uint32_t rr = 4 * (2 * (g & 1) + ((i16 & 3) >> 1));
 #pragma unroll
     for (int tp = 0; tp < 2; tp++)
 #pragma unroll
-      for (int db = 0; db < MLA_DB; db++) {
-        const int imm = 16 * tp * MLA_LROWB + 256 * (db >> 2);
-        const i32x2_t lo = lds_tr16(kt + voff[0][db & 3] + imm);
-        const i32x2_t hi = lds_tr16(kt + voff[1][db & 3] + imm);
-        o[db] = mfma32x32x16_bf16(cat(lo, hi), pb[tp], o[db]);
-        if (db % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-      }
-  };
+      for (int u = 0; u < 2; u++)
+        voff[tp][u] = (8 * wave + (g & 1)) * 1024 + ((i16 & 3) >> 1) * 512 + 8 * (i16 & 1) +
+                      ((16 * tp + 8 * u + 4 * (g >> 1) + (i16 >> 2) + rr) & 31) * 16;
+  }
+  FA_LDS int* const grow_own = (FA_LDS int*)&grow_s[0][lane][wave];
 
-  issue(0, st[0]);
-  if (1 < n_tiles) issue(1, st[1]);
-  for (int t = 0; t < n_tiles; t += 3) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 >= n_tiles) break;
-    tile(std::integral_constant<int, 1>{}, t + 1);
-    if (t + 2 >= n_tiles) break;
-    tile(std::integral_constant<int, 2>{}, t + 2);
+  // Softmax reference of head h, fixed at the first tile of a pass: P = 2^((s - m_ref) c)
+  // stays below 2^kMlaGrow (bf16 keeps its relative precision at any size, and the fp32 sums
+  // stay far from overflow), so O is never rescaled.  A tile whose scores outgrow that bound
+  // makes the workgroup pass over the split again with the reference raised to that tile's
+  // maximum (each such pass raises it by more than kMlaGrow / c, at a later tile).
+  float m_ref = -INFINITY, l = 0.f;
+  // O^T of output columns 128 wave .. +127 for every head: o[d][g] is output block d (32
+  // columns) of head group g
+  f32x16_t o[MLA_OB][MLA_BW];
+  for (;;) {  // passes over the split: one, unless a tile outgrows the reference
+#pragma unroll
+    for (int d = 0; d < MLA_OB; d++)
+#pragma unroll
+      for (int g = 0; g < MLA_BW; g++) o[d][g] = f32x16_t{};
+    l = 0.f;
+    bool grew = false;
+    float mx = 0.f;
+    // Tile t sits in stage t % 3.  Iteration t (0 .. n_tiles) computes the scores of tile t,
+    // then the PV product of tile t-1 with the softmax of tile t woven into it, so that the
+    // exponentials run under the matrix products.  The ends cost a little idle work instead
+    // of code of their own: at t = 0 the product reads tile 0's V against a zero P^T slot
+    // (it adds exactly zero), and at t = n_tiles the scores are all masked (P = 0, no growth).
+    {
+      const Copy c0 = plan_copy(0, 0);
+#pragma unroll
+      for (int k = 0; k < MLA_CPW; k++) copy(c0, k);
+#pragma unroll
+      for (int tp = 0; tp < 2; tp++) *(FA_LDS i32x4_t*)(pt + (2 * MLA_BW + 2 * wave + tp) * 1024 + lane * 16) = i32x4_t{0, 0, 0, 0};
+      grow_own[64 * MLA_BW] = 0;  // tile "-1" (parity 1)
+    }
+    int stc = 0;
+    for (int t = 0; t <= n_tiles; t++) {
+      // tile t landed; every wave is done with tile t-2 (whose stage takes tile t+1), has
+      // written the P^T and growth flag of tile t-1 and has read those of tile t-2
+      wait_vmcnt<0>();
+      wait_lgkmcnt0();
+      barrier();
+      const int stn = stc == 2 ? 0 : stc + 1;
+      const int stp = t == 0 ? stc : (stn == 2 ? 0 : stn + 1);
+      const Copy cn = plan_copy(t + 1, stn);
+      // S^T of this wave's 32 heads over the whole depth, the K reads one group of four steps
+      // ahead of their products; the copies of tile t+1 go out one per group, so that no
+      // wave stalls on a burst of them
+      const FA_LDS char* kt = ring + stc * MLA_CTILE;
+      auto kread = [&](int i) { return lds_b128(kt + ((i & 1) ? koff1 : koff0) + 1024 * i); };
+      f32x16_t s{};
+      i32x4_t kr[2][4];
+#pragma unroll
+      for (int j = 0; j < 4; j++) kr[0][j] = kread(j);
+#pragma unroll
+      for (int gi = 0; gi < MLA_QS / 4; gi++) {
+        if (gi + 1 < MLA_QS / 4) {
+#pragma unroll
+          for (int j = 0; j < 4; j++) kr[(gi + 1) & 1][j] = kread(4 * (gi + 1) + j);
+        }
+        copy(cn, gi);
+#pragma unroll
+        for (int j = 0; j < 4; j++) s = mfma32x32x16_bf16(kr[gi & 1][j], qf[4 * gi + j], s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // register v holds key 8(v/4) + 4hl + v%4 of the tile; keys past the split are masked
+      const int key0 = start + t * TK;
+      if (key0 + TK > end) {
+        const int lim = end - key0 - 4 * hl;
+#pragma unroll
+        for (int v = 0; v < 16; v++) s[v] = (8 * (v >> 2) + (v & 3)) < lim ? s[v] : -INFINITY;
+      }
+      // O^T += V^T P^T of tile t-1, the V^T operands two (tp, d) pairs ahead of their four
+      // products; slice k of the softmax of tile t after pair k: row maximum, growth flag,
+      // exponentials, bf16 P^T with its row sum, P^T into the slot of tile t
+      const FA_LDS char* vt = ring + stp * MLA_CTILE;
+      const int u = (t - 1) & 1;
+      i32x4_t pb[2][MLA_BW];
+#pragma unroll
+      for (int tp = 0; tp < 2; tp++)
+#pragma unroll
+        for (int g = 0; g < MLA_BW; g++) pb[tp][g] = lds_b128(pt + (u * 2 * MLA_BW + 2 * g + tp) * 1024 + lane * 16);
+      // tile t-1 outgrew the reference: pass again (its product has not been taken)
+      const i32x4_t gflag = *(const FA_LDS i32x4_t*)&grow_s[(t - 1) & 1][0][0];
+      if (gflag[0] | gflag[1] | gflag[2] | gflag[3]) {  // uniform over the workgroup; rare
+        grew = true;
+        break;
+      }
+      auto vread = [&](int pi) {
+        const int tp = pi / MLA_OB, d = pi % MLA_OB;
+        return cat(lds_tr16(vt + voff[tp][0] + 2048 * d), lds_tr16(vt + voff[tp][1] + 2048 * d));
+      };
+      float neg = 0.f;
+      i32x4_t pw[2];
+      i32x4_t va[3];
+      va[0] = vread(0);
+      va[1] = vread(1);
+#pragma unroll
+      for (int pi = 0; pi < 2 * MLA_OB; pi++) {
+        if (pi + 2 < 2 * MLA_OB) va[(pi + 2) % 3] = vread(pi + 2);
+        const int tp = pi / MLA_OB, d = pi % MLA_OB;
+#pragma unroll
+        for (int g = 0; g < MLA_BW; g++) o[d][g] = mfma32x32x16_bf16(va[pi % 3], pb[tp][g], o[d][g]);
+        if (pi == 0) {
+          mx = s[0];
+#pragma unroll
+          for (int v = 1; v < 16; v++) mx = fmaxf(mx, s[v]);
+        } else if (pi == 1) {
+          mx = xor32_max(mx);
+          m_ref = t == 0 ? fmaxf(m_ref, mx) : m_ref;  // O and l are still zero at t = 0
+          const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+          neg = -m_use * c;
+          grow_own[(t & 1) * 64 * MLA_BW] = __builtin_amdgcn_ballot_w64(mx * c + neg > kMlaGrow) != 0;
+        } else if (pi < 6) {
+#pragma unroll
+          for (int v = 0; v < 4; v++) s[4 * (pi - 2) + v] = exp2_fast(fmaf(s[4 * (pi - 2) + v], c, neg));
+        } else if (pi == 6) {
+#pragma unroll
+          for (int tp2 = 0; tp2 < 2; tp2++) {
+            pw[tp2] = i32x4_t{pack_bf16(s[8 * tp2], s[8 * tp2 + 1]), pack_bf16(s[8 * tp2 + 2], s[8 * tp2 + 3]),
+                              pack_bf16(s[8 * tp2 + 4], s[8 * tp2 + 5]), pack_bf16(s[8 * tp2 + 6], s[8 * tp2 + 7])};
+#pragma unroll
+            for (int i = 0; i < 4; i++) l = dot2_bf16(pw[tp2][i], kBf16PairOne, l);
+          }
+        } else {
+#pragma unroll
+          for (int tp2 = 0; tp2 < 2; tp2++)
+            *(FA_LDS i32x4_t*)(pt + ((t & 1) * 2 * MLA_BW + 2 * wave + tp2) * 1024 + lane * 16) = pw[tp2];
+        }
+        // each product followed by a share of the slice's vector work, which then runs under it
+#pragma unroll
+        for (int g = 0; g < MLA_BW; g++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // up to five VALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stc = stn;
+    }
+    wait_vmcnt<0>();  // no copy may land in LDS after the workgroup ends
+    if (!grew) break;
+    m_ref = fmaxf(m_ref, mx);  // mx: the maximum of the tile that outgrew the reference
+    barrier();                 // every wave has read the flags and is done with every stage
   }
 
   const float l_tot = xor32_sum(l);
-  if (hvalid) {
+  if (hl == 0 && hvalid) {
     const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + split;
-    float* po = a.part_o + pidx * MLA_DV + 256 * hh + 4 * hl;
-    // O^T register v of block db holds output column 256hh + 32db + 8(v/4) + 4hl + v%4
+    a.part_ml[2 * pidx] = m_ref;
+    a.part_ml[2 * pidx + 1] = l_tot;
+  }
+  // O^T register v of block (d, g) holds output column 128 wave + 32d + 8(v/4) + 4hl + v%4 of
+  // head 32g + l32
 #pragma unroll
-    for (int db = 0; db < MLA_DB; db++)
+  for (int g = 0; g < MLA_BW; g++) {
+    const int hg = 32 * g + l32;
+    if (hg < a.Hq) {
+      const size_t pidx = ((size_t)b * a.Hq + hg) * a.n_split + split;
+      float* po = a.part_o + pidx * MLA_DV + 128 * wave + 4 * hl;
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        *(f32x4_t*)(po + 32 * db + 8 * j) = f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
-    if (hh == 0 && hl == 0) {
-      a.part_ml[2 * pidx] = m_ref;
-      a.part_ml[2 * pidx + 1] = l_tot;
+      for (int d = 0; d < MLA_OB; d++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+          *(f32x4_t*)(po + 32 * d + 8 * j) = f32x4_t{o[d][g][4 * j], o[d][g][4 * j + 1], o[d][g][4 * j + 2], o[d][g][4 * j + 3]};
     }
   }
 }
@@ -739,10 +814,9 @@ __device__ __forceinline__ uint32_t m8_chunk(uint32_t row, uint32_t q) { return 
 __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0_raw[M8_STAGE];
   __shared__ __attribute__((aligned(1024))) char st1_raw[M8_STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2_raw[M8_STAGE];
   __shared__ __attribute__((aligned(1024))) char xs_raw[MLA_NW * 4096];  // partial S^T per wave
   __shared__ __attribute__((aligned(1024))) char dummy_raw[1024];         // target of spare copies
-  FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw, (FA_LDS char*)st2_raw};
+  FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw};
 
   int split, b;
   if (!mla_item(a, split, b)) return;  // uniform over the workgroup
@@ -821,10 +895,9 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
 
   auto tile = [&](auto SLOT, int t) {
     constexpr int sl = decltype(SLOT)::value;
-    if (t + 1 < n_tiles) wait_vmcnt<M8_OPS>();
-    else wait_vmcnt<0>();
+    wait_vmcnt<0>();  // two stages, as in the bf16 kernel
     barrier();
-    if (t + 2 < n_tiles) issue(t + 2, st[(sl + 2) % MLA_NS]);
+    if (t + 1 < n_tiles) issue(t + 1, st[sl ^ 1]);
     const FA_LDS char* kt = st[sl];
     f32x16_t s{};
 #pragma unroll
@@ -890,13 +963,10 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
   };
 
   issue(0, st[0]);
-  if (1 < n_tiles) issue(1, st[1]);
-  for (int t = 0; t < n_tiles; t += 3) {
+  for (int t = 0; t < n_tiles; t += 2) {
     tile(std::integral_constant<int, 0>{}, t);
     if (t + 1 >= n_tiles) break;
     tile(std::integral_constant<int, 1>{}, t + 1);
-    if (t + 2 >= n_tiles) break;
-    tile(std::integral_constant<int, 2>{}, t + 2);
   }
 
   const float l_tot = xor32_sum(l);
@@ -1037,7 +1107,7 @@ hipError_t launch_gqa_decode_static(DecodeArgs a, int D, bool fp8, hipStream_t s
 hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
   const int grid = a.n_split * ((a.B + 7) / 8 * 8);  // see mla_item
   if (fp8) mla_decode_split_fp8<<<grid, 64 * MLA_NW, 0, s>>>(a);
-  else mla_decode_split<<<grid, 64 * MLA_NW, 0, s>>>(a);
+  else mla_decode_split<<<grid, 64 * MLA_BW, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   combine_kernel<<<(a.B * a.Hq * (MLA_DV / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, MLA_DV);

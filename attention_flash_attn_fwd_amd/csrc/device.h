@@ -196,6 +196,21 @@ __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, FA_LDS char*
 __device__ __forceinline__ void dma4_buf(__amdgpu_buffer_rsrc_t r, FA_LDS char* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)lds, 4, voff, 0, 0, 0);
 }
+// The same 16-byte copy issued from inline asm, with the descriptor as four scalar words.
+// The compiler does not track it: it adds no wait of its own before later LDS reads (it
+// cannot tell which stage of a ring a copy writes), so the caller waits with wait_vmcnt
+// and synchronises before reading the destination.  One wait state between the M0 write
+// and the copy that reads it.
+__device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  return i32x4_t{(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+__device__ __forceinline__ void dma16_asm(const i32x4_t& rsrc, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).

@@ -7,6 +7,7 @@ import attention_flash_attn_fwd_amd as fa
 import oracle
 from tests.helpers import BF16_TOL, E4M3_CACHE_TOL, assert_close, assert_lse_close, dev, dev_bf16, host_f64, say
 from workloads import make_decode, make_mla_decode, workload
+from workloads.encode import bf16_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -132,6 +133,31 @@ def test_mla_decode_full_workload_sampled():
     ro, rl = oracle.mla_decode(host_f64(q[picks]), host_f64(kv[picks]), np.full(3, 4096), 512, w.scale)
     assert_close(host_f64(o[picks]), ro, BF16_TOL, "O sampled")
     assert_lse_close(lse[picks].cpu().numpy(), rl, "LSE sampled")
+
+
+def test_mla_decode_growing_scores():
+    """Scores that climb steeply along each sequence: the 64 rope columns of every key are a
+    ramp times one direction that all queries share (plus noise), so each split of 8 tiles
+    sees its scores grow by hundreds of log2 units (the kernel passes over such a split again
+    with a higher softmax reference).  V (the first 512 columns) stays small noise.  Checked
+    against the oracle."""
+    B, H, L = 64, 16, 1024
+    rng = np.random.default_rng(11)
+    u = rng.standard_normal(64)
+    q = rng.standard_normal((B, H, 576))
+    q[..., 512:] = u
+    kv = 0.5 * rng.standard_normal((B, L, 576))
+    kv[..., 512:] += (330.0 * np.arange(L) / L)[None, :, None] * u
+    lens = np.full(B, L, np.int32)
+    lens[1], lens[2] = 1000, 777
+    qd, kvd = dev_bf16(bf16_bits(q.astype(np.float32))), dev_bf16(bf16_bits(kv.astype(np.float32)))
+    scale = 576 ** -0.5
+    say(f"case mla decode growing scores B={B} H={H} L={L}")
+    o, lse = fa.mla_decode(qd, kvd, dev(lens), dv=512, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode(host_f64(qd), host_f64(kvd), lens, 512, scale)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
 
 
 # ------------------------------------------------------------------------------------------
