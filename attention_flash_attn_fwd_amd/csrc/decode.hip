@@ -685,7 +685,8 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
       }
       // register v holds key 8(v/4) + 4hl + v%4 of the tile; keys past the split are masked
       const int key0 = start + t * TK;
-      if (key0 + TK > end) {
+      if (key0 + TK > end) {  // the last tiles only: a branch, not selects on every tile
+        asm volatile("" ::: "memory");
         const int lim = end - key0 - 4 * hl;
 #pragma unroll
         for (int v = 0; v < 16; v++) s[v] = (8 * (v >> 2) + (v & 3)) < lim ? s[v] : -INFINITY;
@@ -804,7 +805,7 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
 constexpr int M8_ROWB = 576;                         // e4m3 latent row
 constexpr int M8_TILE = TK * M8_ROWB;                // 18 KiB per stage
 constexpr int M8_BLKS = M8_TILE / 1024;              // 18 one-KiB direct copies per tile
-constexpr int M8_OPS = (M8_BLKS + MLA_NW - 1) / MLA_NW;  // 3 per wave (spare slots: scales, dummy)
+constexpr int M8_OPS = (M8_BLKS + MLA_NW - 1) / MLA_NW;  // 3 per wave (wave 2's third: the scales)
 constexpr int M8_SC = 256;                           // scale copy: 64 lanes x 4 bytes
 constexpr int M8_STAGE = M8_TILE + M8_SC;
 constexpr int M8_KR = MLA_DK / 32 / 2;               // 16-byte K reads per wave per tile (9)
@@ -815,7 +816,6 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char st0_raw[M8_STAGE];
   __shared__ __attribute__((aligned(1024))) char st1_raw[M8_STAGE];
   __shared__ __attribute__((aligned(1024))) char xs_raw[MLA_NW * 4096];  // partial S^T per wave
-  __shared__ __attribute__((aligned(1024))) char dummy_raw[1024];         // target of spare copies
   FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw};
 
   int split, b;
@@ -844,12 +844,14 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
   const char* kv = (const char*)a.k + (size_t)b * a.max_len * M8_ROWB;
   const float* ksb = a.k_scale + (size_t)b * a.max_len;
   // direct copies of a tile: block blk < 18 of LDS bytes [1024 blk, +1024) is row o / 576,
-  // physical chunk (o % 576) / 16 for o = 1024 blk + 16 lane; the spare third copy of
-  // wave 2 brings the tile's row scales, the other spares (offset out of range, so nothing
-  // is fetched) land in a dummy buffer, so every wave issues the same number of copies per tile
+  // physical chunk (o % 576) / 16 for o = 1024 blk + 16 lane; wave 2 also brings the tile's
+  // row scales.  Issued from inline asm: the compiler, unable to tell which stage a copy
+  // writes, would otherwise wait for the copies of the next tile before this tile's LDS
+  // reads; each tile starts with an explicit wait for every copy and a barrier instead.
   auto issue = [&](int t, FA_LDS char* dst) {
     const int key0 = start + t * TK, valid = min(TK, end - key0);
-    const auto r = make_rsrc(kv + (size_t)key0 * M8_ROWB, (uint32_t)valid * M8_ROWB);
+    const i32x4_t r = rsrc_words(kv + (size_t)key0 * M8_ROWB, (uint32_t)valid * M8_ROWB);
+    const uint32_t dst_lds = lds_addr(dst);
 #pragma unroll
     for (int i = 0; i < M8_OPS; i++) {
       const int blk = i * MLA_NW + wave;
@@ -857,12 +859,10 @@ __global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
         const uint32_t o = blk * 1024 + lane * 16;
         const uint32_t row = o / M8_ROWB, pc = (o % M8_ROWB) >> 4;
         const uint32_t rc = min(row, (uint32_t)(valid - 1));  // rows past the sequence repeat its last row
-        dma16_buf(r, dst + blk * 1024, rc * M8_ROWB + m8_chunk(row, pc) * 16);
+        dma16_asm(r, dst_lds + blk * 1024, rc * M8_ROWB + m8_chunk(row, pc) * 16);
       } else if (blk == M8_BLKS) {
-        const auto rs = make_rsrc(ksb + key0, (uint32_t)valid * 4);
-        dma4_buf(rs, dst + M8_TILE, (uint32_t)min(lane, valid - 1) * 4);
-      } else {
-        dma16_buf(r, (FA_LDS char*)dummy_raw, kOutOfRange);
+        const i32x4_t rs = rsrc_words(ksb + key0, (uint32_t)valid * 4);
+        dma4_asm(rs, dst_lds + M8_TILE, (uint32_t)min(lane, valid - 1) * 4);
       }
     }
   };

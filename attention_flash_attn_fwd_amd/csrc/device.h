@@ -211,6 +211,12 @@ __device__ __forceinline__ void dma16_asm(const i32x4_t& rsrc, uint32_t lds_byte
                : "s"(lds_byte), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+__device__ __forceinline__ void dma4_asm(const i32x4_t& rsrc, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
