@@ -765,8 +765,13 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
   }
 
   const float l_tot = xor32_sum(l);
-  if (hl == 0 && hvalid) {
-    const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + split;
+  // The output addresses are formed here from a fresh lane index (an asm the compiler cannot
+  // hoist), so that nothing computed before the loop stays live across it.
+  int lane_e;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+  const int l32e = lane_e & 31, hle = lane_e >> 5;
+  if (hle == 0 && 32 * wave + l32e < a.Hq) {
+    const size_t pidx = ((size_t)b * a.Hq + 32 * wave + l32e) * a.n_split + split;
     a.part_ml[2 * pidx] = m_ref;
     a.part_ml[2 * pidx + 1] = l_tot;
   }
@@ -774,10 +779,10 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
   // head 32g + l32
 #pragma unroll
   for (int g = 0; g < MLA_BW; g++) {
-    const int hg = 32 * g + l32;
+    const int hg = 32 * g + l32e;
     if (hg < a.Hq) {
       const size_t pidx = ((size_t)b * a.Hq + hg) * a.n_split + split;
-      float* po = a.part_o + pidx * MLA_DV + 128 * wave + 4 * hl;
+      float* po = a.part_o + pidx * MLA_DV + 128 * wave + 4 * hle;
 #pragma unroll
       for (int d = 0; d < MLA_OB; d++)
 #pragma unroll
@@ -785,6 +790,7 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
           *(f32x4_t*)(po + 32 * d + 8 * j) = f32x4_t{o[d][g][4 * j], o[d][g][4 * j + 1], o[d][g][4 * j + 2], o[d][g][4 * j + 3]};
     }
   }
+
 }
 
 // ------------------------------------------------------------------------------------
