@@ -137,9 +137,9 @@ struct QkBf16 {
 // MLA prefill with per-token scales: nope (Dn = 128) in e4m3 or bf16, rope (Dr = 64) bf16
 // with Hr rope heads, fp32 q_scale per query row and k_scale per key.
 // K part of a stage: k_nope [BN][Dn] | k_rope [BN][64] bf16 | k_scale [BN] fp32.
-template <bool FP8>
+template <bool FP8, int NW_ = 4>
 struct QkMla {
-  static constexpr int NW = 4;
+  static constexpr int NW = NW_;  // waves of the workgroup that share the copies
   static constexpr int NROWB = FP8 ? 128 : 256;
   static constexpr int KN = 0;
   static constexpr int KR = BN * NROWB;
@@ -153,8 +153,8 @@ struct QkMla {
     float qs;
   };
   struct Lane {
-    RowDma<NROWB> ndma;
-    RowDma<128> rdma;
+    RowDma<NROWB, DefaultSwz<NROWB>, NW> ndma;
+    RowDma<128, DefaultSwz<128>, NW> rdma;
     uint32_t na[NNA];  // nope chunk offsets
     uint32_t ra[4];    // rope chunk offsets
     uint32_t sa;       // k_scale offset of this lane's first key
@@ -626,15 +626,20 @@ hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, int D, hipStream_t s
 
 template <class QK, class VP>
 void launch_mla(const PrefillArgs& a, int grid, int nqb, hipStream_t s) {
-  if (a.causal) prefill_kernel<QK, VP, true><<<grid, 256, 0, s>>>(a, nqb);
-  else prefill_kernel<QK, VP, false><<<grid, 256, 0, s>>>(a, nqb);
+  if (a.causal) prefill_kernel<QK, VP, true><<<grid, 64 * QK::NW, 0, s>>>(a, nqb);
+  else prefill_kernel<QK, VP, false><<<grid, 64 * QK::NW, 0, s>>>(a, nqb);
 }
 
 hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, bool v_fp8, hipStream_t s) {
   int nqb;
-  const int grid = items(a, 128, nqb);
+  // e4m3 nope with bf16 V, causal, from 2048 query rows: 8 waves and 256 query rows per
+  // workgroup, sharing each K/V tile copy between twice the rows (as the bf16 prefill)
+  const bool wide = nope_fp8 && !v_fp8 && a.causal && a.Sq >= 2048;
+  const int grid = items(a, wide ? 256 : 128, nqb);
   if (grid == 0) return hipSuccess;
-  if (nope_fp8) {
+  if (wide) {
+    launch_mla<QkMla<true, 8>, VBf16<128, 8>>(a, grid, nqb, s);
+  } else if (nope_fp8) {
     if (v_fp8) launch_mla<QkMla<true>, VE4m3<128>>(a, grid, nqb, s);
     else launch_mla<QkMla<true>, VBf16<128>>(a, grid, nqb, s);
   } else {

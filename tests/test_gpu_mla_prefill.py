@@ -186,6 +186,7 @@ MLA_BATCHED = [
     (3, 64, 200, 2, 2, False, True, True, False),     # bf16 nope, e4m3 V, non-causal
     (2, 96, 257, 2, 1, True, False, False, True),     # e4m3 nope without scales
     (2, 300, 300, 2, 1, True, True, False, True),     # Sq = Skv across two sequences
+    (2, 2080, 2200, 2, 1, True, True, False, True),   # long causal rows: 256-row blocks, ragged tail
 ]
 
 
