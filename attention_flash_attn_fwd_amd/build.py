@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "prefill.hip", "prefill_f32.hip", "decode.hip", "merge.hip", "quantize.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "prefill.hip", "prefill_w64.hip", "prefill_f32.hip", "decode.hip", "merge.hip", "quantize.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

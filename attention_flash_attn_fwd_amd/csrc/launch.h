@@ -67,6 +67,9 @@ struct QuantArgs {
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s);
+// bf16 MHA / GQA prefill of head dim 128 without the causal mask: 64 query rows per wave, one
+// wave per SIMD.
+hipError_t launch_prefill_w64(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_prefill_varlen_bf16(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, bool v_fp8, hipStream_t s);

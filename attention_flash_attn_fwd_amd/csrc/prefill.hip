@@ -590,6 +590,15 @@ int items(const PrefillArgs& a, int bm, int& n_qblocks) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t s) {
+  // Head dim 128 without the causal mask, over at least 2048 keys and with at least one
+  // 256-row block per CU: 64 query rows per wave, one wave per SIMD (5-6 % faster on B4 H32
+  // S4096, also with 8 kv heads, and on B8 S256/2048; slower with shorter key ranges, where
+  // each block's pipeline fill and drain weigh more, and with fewer blocks than CUs).  Also
+  // needs a (batch, kv head)'s key rows plus the tiles the pipeline runs ahead to span less
+  // than 2^31 bytes (32-bit lane offsets into one buffer range).
+  if (D == 128 && !a.causal && a.Skv >= 2048 && (size_t)a.B * a.Hq * ((a.Sq + 255) / 256) >= 256 &&
+      (size_t)(a.Skv + 256) * (size_t)a.Hkv * 256 < (size_t(1) << 31))
+    return launch_prefill_w64(a, s);
   int nqb;
   // 8 waves per workgroup measured 2-3 % faster for causal head dim 128 from 2048 query rows
   // on (slower for head dim 64 and without the causal mask)

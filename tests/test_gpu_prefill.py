@@ -163,3 +163,45 @@ def test_bf16_first_causal_row_is_v0_and_identical_v_rows(D):
         torch.cuda.synchronize()
         ref = np.broadcast_to(np.repeat(host_f64(v[:, 7:8]), 2, axis=2), o.shape)
         assert_close(host_f64(o), ref, BF16_TOL, f"identical V rows causal={causal}")
+
+
+# Without the causal mask, head dim 128 over at least 2048 keys and at least 256 blocks of 256
+# query rows runs the kernel with 64 query rows per wave; these cases take that path.
+W64_CASES = [
+    # B, Sq, Skv, Hq, Hkv
+    (2, 260, 2100, 64, 8),    # ragged last query block and last key tile, GQA group of 8
+    (1, 513, 2048, 128, 128),  # whole key tiles, three blocks with a ragged last one
+    (8, 256, 2049, 32, 32),   # one key past a whole tile
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv", W64_CASES)
+def test_bf16_noncausal_long_keys(B, Sq, Skv, Hq, Hkv):
+    w = workload("mha_prefill_causal_bf16_b4_h32_s4096_d128", B=B, Sq=Sq, Skv=Skv, Hq=Hq, Hkv=Hkv, causal=False)
+    _check_full(w, BF16_TOL)
+
+
+@pytest.mark.parametrize("climb", [0.6, 4.0])
+def test_bf16_noncausal_growing_scores(climb):
+    """Scores that climb along the keys: every query and key row carries a shared direction,
+    the keys with a weight that ramps from 0 to CLIMB.  At 0.6 the last keys' logits exceed the
+    first tile's by about 30 log2 units; at 4.0 by about 200, far past what an fp32 sum of
+    exponentials against the first tile's maximum can hold, which the 64-row kernel detects and
+    answers with a second pass at the exact row maxima.  Checked against the oracle.  V is
+    N(0, 1/4): at 0.6 each row's weight sits on a few dozen keys, so the one bf16 rounding of
+    every P value moves O by up to about 2^-9 |V - O|; emulating exactly that rounding in fp64
+    on N(0,1) V gives 9.2e-3, at the edge of the 1e-2 bar, for any kernel that multiplies V by
+    bf16 P."""
+    B, Sq, Skv, H = 2, 300, 2100, 64
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, Sq, H, 128)) + 3.0
+    k = rng.standard_normal((B, Skv, H, 128)) + (climb * np.arange(Skv) / Skv)[None, :, None, None]
+    v = 0.5 * rng.standard_normal((B, Skv, H, 128))
+    qd, kd, vd = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for x in (q, k, v))
+    scale = 128 ** -0.5
+    say(f"case growing scores climb={climb} B={B} Sq={Sq} Skv={Skv} H={H}")
+    o, lse = fa.prefill(qd, kd, vd, causal=False, scale=scale, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill(host_f64(qd), host_f64(kd), host_f64(vd), scale, False)
+    assert_close(host_f64(o), ro, BF16_TOL, "O")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE")
