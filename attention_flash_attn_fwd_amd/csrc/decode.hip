@@ -502,46 +502,57 @@ __global__ __launch_bounds__(64) void gqa_decode_split_fp8(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// MLA decode split: one workgroup of 8 waves per (split, batch).  The heads form four
-// groups of 32 -- the N columns of v_mfma_f32_32x32x16_bf16 -- and each group is served by
-// the pair of waves w, w + 4 that share a SIMD.  For S^T = K.Q^T the pair splits the
-// 576-deep contraction: wave half hh = w / 4 takes the 16-column steps 2i + hh, and the two
-// partial S^T meet through LDS (the sum is formed identically by both waves).  For
-// O^T = V^T.P^T the pair splits the 512 output columns (hh selects 256 of them).  So a
-// wave keeps half of Q^T (72 VGPRs) and half of O^T (128), and every 16-byte K read or
-// 8-byte transposed V read feeds a 32x32 product.  The 576-wide latent tile (32 keys) is
-// copied once per workgroup into a two-stage LDS ring by direct loads; its first 512
-// columns are V, so the cache is read from HBM once.
+// MLA decode split: one workgroup of 4 waves -- one per SIMD, 512 registers each -- per
+// (split, batch).  The heads form four groups of 32, the N columns of
+// v_mfma_f32_32x32x16_bf16.  Wave w computes S^T = K.Q^T for head group w over the whole
+// 576-deep contraction (its Q^T in 144 VGPRs), runs that group's softmax and writes its bf16
+// P^T to LDS; then it takes O^T += V^T.P^T for output columns 128w .. 128w+127 of all 128
+// heads (O^T in the 256 AGPRs), so each V^T operand read from LDS feeds four products.  The
+// 576-wide latent tile (32 keys) is copied once per workgroup into a three-stage LDS ring by
+// direct loads; its first 512 columns are V, so the cache is read from HBM once.
 //
-// LDS tile layout ("chunk-column major"): 16-byte chunk c (8 latent columns) of key row r
-// sits at (c / 2) * 1024 + (c % 2) * 512 + ((r + 4 (c % 4)) % 32) * 16, i.e. each 1 KiB block
-// holds two chunk columns of all 32 rows, each column rotated by 4 (c % 4) row slots.  Then a
-// direct copy instruction moves one whole block (lane l: row slot l % 32 of column 2j + l / 32,
-// a source offset of one of two per-lane patterns plus 32 j), the K read of a contraction step
-// is one contiguous 1 KiB block, and the transposing V reads of a pass hit 16 distinct 16-byte
-// slots (all 64 banks once): no padding, and a handful of address registers.
+// bf16 cache, LDS tile layout ("chunk-column major"): 16-byte chunk c (8 latent columns) of
+// key row r sits at (c / 2) * 1024 + (c % 2) * 512 + ((r + 4 (c % 4)) % 32) * 16, i.e. each
+// 1 KiB block holds two chunk columns of all 32 rows, each column rotated by 4 (c % 4) row
+// slots.  Then a direct copy instruction moves one whole block (lane l: row slot l % 32 of
+// column 2j + l / 32, a source offset of one of two per-lane patterns plus 32 j), the K read
+// of a contraction step is one contiguous 1 KiB block, and the transposing V reads of a pass
+// hit 16 distinct 16-byte slots (all 64 banks once): no padding, and a handful of address
+// registers.
+//
+// e4m3 cache with one fp32 scale per cache row (kv_scale [B, max_len]; the row serves as K
+// and, through its first 512 columns, as V, so K = code * scale and V = code[:512] * scale):
+//  * LDS rows are the 576 code bytes, unpadded; 16-byte chunk q of row r sits at chunk
+//    q ^ ((r >> 2) & 3) (within its aligned group of four), which keeps both read patterns
+//    free of bank conflicts; the tile's 32 row scales follow the codes;
+//  * S^T A operand: one 16-byte read gives a lane 16 consecutive latent columns, i.e. its
+//    halves of two 32x32x16 steps (the contraction order is permuted: block p, lane half hl,
+//    step u, element i is column 32p + 16hl + 8u + i, and Q^T uses the same order), so a
+//    wave issues half the K reads of the bf16 cache;
+//  * V^T A operand: one ds_read_b64_tr_b8 per product (8 keys of one column per lane);
+//  * codes convert exactly to bf16; the row scale multiplies S and is folded into P.
 
-constexpr int MLA_DK = 576, MLA_DV = 512, MLA_ROWB = 1152, MLA_LROWB = 1280;
-constexpr int MLA_CTILE = TK * MLA_ROWB;              // 36 KiB per stage (bf16 kernel)
+constexpr int MLA_DK = 576, MLA_DV = 512, MLA_ROWB = 1152;
+constexpr int MLA_CTILE = TK * MLA_ROWB;              // 36 KiB per stage (bf16 cache)
 constexpr int MLA_CBLK = MLA_CTILE / 1024;            // 36 one-KiB copy blocks per tile
-constexpr int MLA_LTILE = TK * MLA_LROWB;             // 40 KiB (row-padded tiles of the e4m3 kernel's scale path)
-constexpr int MLA_NW = 8, MLA_NS = 2;
-constexpr int MLA_OPS = MLA_LTILE / 1024 / MLA_NW;    // direct copies per wave per tile (e4m3 kernel)
-constexpr int MLA_KS = MLA_DK / 32;                   // contraction steps per wave (18)
-constexpr int MLA_DB = MLA_DV / 64;                   // 32-column output blocks per wave (8)
-constexpr int MLA_BW = 4;                             // waves of the bf16 kernel (one per SIMD)
-constexpr int MLA_QS = MLA_DK / 16;                   // its S contraction steps per wave (36)
-constexpr int MLA_OB = MLA_DV / 32 / MLA_BW;          // its 32-column output blocks per wave (4)
+constexpr int MLA_BW = 4;                             // waves (one per SIMD)
+constexpr int MLA_QS = MLA_DK / 16;                   // S contraction steps per wave (36)
+constexpr int MLA_OB = MLA_DV / 32 / MLA_BW;          // 32-column output blocks per wave (4)
 static_assert(MLA_CBLK % MLA_BW == 0 && MLA_BW % 2 == 0, "bf16 tile copy split");
-constexpr int MLA_CPW = MLA_CBLK / MLA_BW;            // its direct copies per wave per tile (9)
+constexpr int MLA_CPW = MLA_CBLK / MLA_BW;            // direct copies per wave per tile, bf16 (9)
 static_assert(MLA_CPW == MLA_QS / 4, "one copy per group of four S steps");
 constexpr float kMlaGrow = 64.f;                      // log2 bound of P against the fixed reference
-static_assert(MLA_LTILE % (1024 * MLA_NW) == 0, "tile copy split");
 
-// physical 16-byte chunk of logical chunk lc in LDS row `row` (row-padded layout)
-__device__ __forceinline__ uint32_t mla_chunk(uint32_t row, uint32_t lc) {
-  return (lc & ~15u) | ((lc & 15u) ^ swz256(row));
-}
+constexpr int M8_ROWB = 576;                          // e4m3 latent row
+constexpr int M8_TILE = TK * M8_ROWB;                 // 18 KiB of codes per tile
+constexpr int M8_BLKS = M8_TILE / 1024;               // 18 one-KiB direct copies per tile
+constexpr int M8_STAGE = M8_TILE + 256;               // codes | row scales
+constexpr int M8_CPW = 5;                             // direct copies per wave per tile, e4m3
+static_assert(M8_BLKS + 1 <= M8_CPW * MLA_BW && 2 * M8_CPW - 1 <= MLA_QS / 4,
+              "the copies cover codes and scales, one per second group of four S steps");
+
+// physical 16-byte chunk of logical chunk q in e4m3 row `row` (an involution)
+__device__ __forceinline__ uint32_t m8_chunk(uint32_t row, uint32_t q) { return q ^ ((row >> 2) & 3u); }
 
 // Work item of an MLA split kernel (one workgroup = one split of one sequence).  The grid
 // is 1-D; workgroup i runs on XCD i % 8.  Every split of sequence b runs on XCD b % 8, at
@@ -555,8 +566,10 @@ __device__ __forceinline__ bool mla_item(const DecodeArgs& a, int& split, int& b
   return b < a.B;
 }
 
+template <bool E8>
 __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char ring_raw[3 * MLA_CTILE];
+  constexpr int STAGE = E8 ? M8_STAGE : MLA_CTILE;  // bytes per ring stage
+  __shared__ __attribute__((aligned(1024))) char ring_raw[3 * STAGE];
   __shared__ __attribute__((aligned(1024))) char pt_raw[2 * MLA_BW * 2 * 1024];  // P^T of two tiles
   // head group whose scores outgrew the reference, per tile parity; lanes other than 0 of a
   // wave write their copy of the flag into a slot of their own (no branch on the lane), so
@@ -579,34 +592,63 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
   const float c = a.scale * kLog2e;
 
   // Q^T of head group `wave` over the whole latent depth, as the B operand: column l32 = head
-  // h; step i covers latent columns 16i + 8hl .. +7
+  // h; step i covers latent columns 16i + 8hl .. +7 (e4m3 cache: step i = 2p + u covers
+  // columns 32p + 16hl + 8u .. +7, the order in which one 16-byte read of a code row gives a
+  // lane its K operands of two steps)
   i32x4_t qf[MLA_QS];
   {
-    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * MLA_ROWB + 16 * hl;
+    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * MLA_ROWB + (E8 ? 32 : 16) * hl;
 #pragma unroll
-    for (int i = 0; i < MLA_QS; i++) qf[i] = *(const i32x4_t*)(qp + 32 * i);
+    for (int i = 0; i < MLA_QS; i++) qf[i] = *(const i32x4_t*)(qp + (E8 ? 64 * (i >> 1) + 16 * (i & 1) : 32 * i));
   }
-  const char* kv = (const char*)a.k + (size_t)b * a.max_len * MLA_ROWB;
+  const char* kv = (const char*)a.k + (size_t)b * a.max_len * (E8 ? M8_ROWB : MLA_ROWB);
   // direct copy k (0 .. 8) of a tile: block j = 4k + wave; lane l fills row slot l % 32 of
   // chunk column 2j + l / 32, i.e. key row (l % 32 - 8 (j % 2) - 4 (l / 32)) mod 32.  Rows past
   // the sequence repeat its last row; past the last tile the copies fetch nothing (an offset
   // beyond the range).
   const uint32_t crow = (uint32_t)(l32 - 8 * (wave & 1) - 4 * hl) & 31u;
   const uint32_t ring_lds = lds_addr(ring) + wave * 1024;
-  struct Copy { i32x4_t r; uint32_t src, dst; };
+  struct Copy { i32x4_t r, rs; uint32_t src, dst; int valid; bool live; };
   auto plan_copy = [&](int t, int stage) {
     const int tt = min(t, n_tiles - 1);
     const int key0 = start + tt * TK, valid = min(TK, end - key0);
     Copy cp;
-    cp.r = rsrc_words(kv + (size_t)key0 * MLA_ROWB, (uint32_t)valid * MLA_ROWB);
-    cp.src = t < n_tiles ? min(crow, (uint32_t)(valid - 1)) * MLA_ROWB + 16u * hl + 32u * wave : kOutOfRange;
-    cp.dst = ring_lds + stage * MLA_CTILE;
+    cp.valid = valid;
+    cp.live = t < n_tiles;
+    if constexpr (E8) {
+      cp.r = rsrc_words(kv + (size_t)key0 * M8_ROWB, (uint32_t)valid * M8_ROWB);
+      cp.rs = rsrc_words(a.k_scale + (size_t)b * a.max_len + key0, (uint32_t)valid * 4);
+      cp.dst = lds_addr(ring) + stage * STAGE;
+    } else {
+      cp.r = rsrc_words(kv + (size_t)key0 * MLA_ROWB, (uint32_t)valid * MLA_ROWB);
+      cp.src = t < n_tiles ? min(crow, (uint32_t)(valid - 1)) * MLA_ROWB + 16u * hl + 32u * wave : kOutOfRange;
+      cp.dst = ring_lds + stage * MLA_CTILE;
+    }
     return cp;
   };
-  auto copy = [&](const Copy& cp, int k) { dma16_asm(cp.r, cp.dst + k * MLA_BW * 1024, cp.src + 32u * MLA_BW * k); };
-  // S^T A operand of step i: key row l32, chunk 2i + hl, at koff[i % 2] + 1024 i
-  const uint32_t koff0 = hl * 512 + ((l32 + 4 * hl) & 31) * 16;
-  const uint32_t koff1 = hl * 512 + ((l32 + 8 + 4 * hl) & 31) * 16;
+  // e4m3 cache: copy k (0 .. M8_CPW-1) of a tile is block j = 4k + wave; block j < 18 holds LDS bytes
+  // [1024 j, +1024) of the code rows (lane l: byte o = 1024 j + 16 l, row o / 576, physical
+  // chunk (o % 576) / 16), block 18 the 32 row scales, block 19 nothing
+  auto copy = [&](const Copy& cp, int k) {
+    if constexpr (E8) {
+      const int j = 4 * k + wave;  // wave-uniform
+      if (j < M8_BLKS) {
+        const uint32_t o = 1024u * j + 16u * lane, row = o / M8_ROWB, pc = (o % M8_ROWB) >> 4;
+        const uint32_t src = min(row, (uint32_t)(cp.valid - 1)) * M8_ROWB + m8_chunk(row, pc) * 16;
+        dma16_asm(cp.r, cp.dst + 1024u * j, cp.live ? src : kOutOfRange);
+      } else if (j == M8_BLKS) {
+        dma4_asm(cp.rs, cp.dst + M8_TILE, cp.live ? (uint32_t)min(lane, cp.valid - 1) * 4 : kOutOfRange);
+      }
+    } else {
+      dma16_asm(cp.r, cp.dst + k * MLA_BW * 1024, cp.src + 32u * MLA_BW * k);
+    }
+  };
+  // S^T A operand of step i: key row l32, chunk 2i + hl, at koff[i % 2] + 1024 i.  e4m3: the
+  // 16-byte read j of group gi is code row l32, logical chunk 4 gi + 2j + hl (steps 4gi + 2j
+  // and + 1), at koff[j] + 64 gi
+  const uint32_t koff0 = E8 ? l32 * M8_ROWB + ((hl ^ ((l32 >> 2) & 3)) << 4) : hl * 512 + ((l32 + 4 * hl) & 31) * 16;
+  const uint32_t koff1 = E8 ? l32 * M8_ROWB + (((2 + hl) ^ ((l32 >> 2) & 3)) << 4)
+                            : hl * 512 + ((l32 + 8 + 4 * hl) & 31) * 16;
   // V^T reads (A operand of O^T) of P^T block tp, half u, output block d of this wave: key
   // rows 16tp + 8u + 4(g/2) + i16/4, output columns 128 wave + 32d + 16(g%2) + 4(i16%4) .. +3
   // (chunk 16 wave + 4d + 2(g%2) + (i16%4)/2), at voff[tp][u] + 2048 d
@@ -620,6 +662,21 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
       for (int u = 0; u < 2; u++)
         voff[tp][u] = (8 * wave + (g & 1)) * 1024 + ((i16 & 3) >> 1) * 512 + 8 * (i16 & 1) +
                       ((16 * tp + 8 * u + 4 * (g >> 1) + (i16 >> 2) + rr) & 31) * 16;
+    if constexpr (E8) {
+      // e4m3: one ds_read_b64_tr_b8 per operand.  16-lane group g (hl = g / 2, column half
+      // dh = g % 2); lane 2e + h of the group reads key row 16tp + 8(e/4) + 4hl + e%4 at byte
+      // 8h of logical chunk 8 wave + 2d + dh, so output byte e of lane l is column
+      // 128 wave + 32d + l%32 of that key -- the P^T key order.  The XOR touches the two low
+      // chunk bits: voff[tp][d % 2] + 64 (d / 2).
+      const uint32_t e = (lane & 15) >> 1, hb = lane & 1;
+#pragma unroll
+      for (int tp = 0; tp < 2; tp++) {
+        const uint32_t row = 16 * tp + 8 * (e >> 2) + 4 * (g >> 1) + (e & 3);
+        const uint32_t x = (g & 1) ^ ((row >> 2) & 3);
+#pragma unroll
+        for (int par = 0; par < 2; par++) voff[tp][par] = row * M8_ROWB + 8 * hb + ((8 * wave + (x ^ (2 * par))) << 4);
+      }
+    }
   }
   FA_LDS int* const grow_own = (FA_LDS int*)&grow_s[0][lane][wave];
 
@@ -648,7 +705,7 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
     {
       const Copy c0 = plan_copy(0, 0);
 #pragma unroll
-      for (int k = 0; k < MLA_CPW; k++) copy(c0, k);
+      for (int k = 0; k < (E8 ? M8_CPW : MLA_CPW); k++) copy(c0, k);
 #pragma unroll
       for (int tp = 0; tp < 2; tp++) *(FA_LDS i32x4_t*)(pt + (2 * MLA_BW + 2 * wave + tp) * 1024 + lane * 16) = i32x4_t{0, 0, 0, 0};
       grow_own[64 * MLA_BW] = 0;  // tile "-1" (parity 1)
@@ -666,24 +723,58 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
       // S^T of this wave's 32 heads over the whole depth, the K reads one group of four steps
       // ahead of their products; the copies of tile t+1 go out one per group, so that no
       // wave stalls on a burst of them
-      const FA_LDS char* kt = ring + stc * MLA_CTILE;
-      auto kread = [&](int i) { return lds_b128(kt + ((i & 1) ? koff1 : koff0) + 1024 * i); };
+      const FA_LDS char* kt = ring + stc * STAGE;
       f32x16_t s{};
-      i32x4_t kr[2][4];
+      if constexpr (E8) {
+        auto kread = [&](int gi, int j) { return lds_b128(kt + (j ? koff1 : koff0) + 64 * gi); };
+        i32x4_t kr[2][2];
 #pragma unroll
-      for (int j = 0; j < 4; j++) kr[0][j] = kread(j);
+        for (int j = 0; j < 2; j++) kr[0][j] = kread(0, j);
 #pragma unroll
-      for (int gi = 0; gi < MLA_QS / 4; gi++) {
-        if (gi + 1 < MLA_QS / 4) {
+        for (int gi = 0; gi < MLA_QS / 4; gi++) {
+          if (gi + 1 < MLA_QS / 4) {
 #pragma unroll
-          for (int j = 0; j < 4; j++) kr[(gi + 1) & 1][j] = kread(4 * (gi + 1) + j);
+            for (int j = 0; j < 2; j++) kr[(gi + 1) & 1][j] = kread(gi + 1, j);
+          }
+          if (gi % 2 == 0) copy(cn, gi / 2);
+#pragma unroll
+          for (int j = 0; j < 2; j++) {
+            const i32x4_t w = kr[gi & 1][j];
+            s = mfma32x32x16_bf16(e4m3x8_to_bf16(i32x2_t{w.x, w.y}), qf[4 * gi + 2 * j], s);
+            s = mfma32x32x16_bf16(e4m3x8_to_bf16(i32x2_t{w.z, w.w}), qf[4 * gi + 2 * j + 1], s);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        copy(cn, gi);
+      } else {
+        auto kread = [&](int i) { return lds_b128(kt + ((i & 1) ? koff1 : koff0) + 1024 * i); };
+        i32x4_t kr[2][4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) s = mfma32x32x16_bf16(kr[gi & 1][j], qf[4 * gi + j], s);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; j++) kr[0][j] = kread(j);
+#pragma unroll
+        for (int gi = 0; gi < MLA_QS / 4; gi++) {
+          if (gi + 1 < MLA_QS / 4) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) kr[(gi + 1) & 1][j] = kread(4 * (gi + 1) + j);
+          }
+          copy(cn, gi);
+#pragma unroll
+          for (int j = 0; j < 4; j++) s = mfma32x32x16_bf16(kr[gi & 1][j], qf[4 * gi + j], s);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      // register v holds key 8(v/4) + 4hl + v%4 of the tile; keys past the split are masked
+      // register v holds key 8(v/4) + 4hl + v%4 of the tile.  e4m3: the row scales of tile t
+      // multiply S (and fold into P below: V = code * scale), before the mask so that a
+      // masked score stays -inf whatever the scale
+      const FA_LDS char* const rscale = kt + M8_TILE + 16 * hl;  // keys 8j + 4hl .. +3 at 32 j
+      if constexpr (E8) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const f32x4_t r = lds_f32x4(rscale + 32 * j);
+#pragma unroll
+          for (int v = 0; v < 4; v++) s[4 * j + v] *= r[v];
+        }
+      }
+      // keys past the split are masked
       const int key0 = start + t * TK;
       if (key0 + TK > end) {  // the last tiles only: a branch, not selects on every tile
         asm volatile("" ::: "memory");
@@ -694,7 +785,7 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
       // O^T += V^T P^T of tile t-1, the V^T operands two (tp, d) pairs ahead of their four
       // products; slice k of the softmax of tile t after pair k: row maximum, growth flag,
       // exponentials, bf16 P^T with its row sum, P^T into the slot of tile t
-      const FA_LDS char* vt = ring + stp * MLA_CTILE;
+      const FA_LDS char* vt = ring + stp * STAGE;
       const int u = (t - 1) & 1;
       i32x4_t pb[2][MLA_BW];
 #pragma unroll
@@ -707,21 +798,28 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
         grew = true;
         break;
       }
-      auto vread = [&](int pi) {
+      // V^T operands as read (e4m3: the eight codes, converted at their products)
+      using VRaw = std::conditional_t<E8, i32x2_t, i32x4_t>;
+      auto vread = [&](int pi) -> VRaw {
         const int tp = pi / MLA_OB, d = pi % MLA_OB;
-        return cat(lds_tr16(vt + voff[tp][0] + 2048 * d), lds_tr16(vt + voff[tp][1] + 2048 * d));
+        if constexpr (E8) return lds_tr8(vt + voff[tp][d & 1] + 64 * (d >> 1));
+        else return cat(lds_tr16(vt + voff[tp][0] + 2048 * d), lds_tr16(vt + voff[tp][1] + 2048 * d));
       };
+
       float neg = 0.f;
       i32x4_t pw[2];
-      i32x4_t va[3];
+      VRaw va[3];
       va[0] = vread(0);
       va[1] = vread(1);
 #pragma unroll
       for (int pi = 0; pi < 2 * MLA_OB; pi++) {
         if (pi + 2 < 2 * MLA_OB) va[(pi + 2) % 3] = vread(pi + 2);
         const int tp = pi / MLA_OB, d = pi % MLA_OB;
+        i32x4_t vop;
+        if constexpr (E8) vop = e4m3x8_to_bf16(va[pi % 3]);
+        else vop = va[pi % 3];
 #pragma unroll
-        for (int g = 0; g < MLA_BW; g++) o[d][g] = mfma32x32x16_bf16(va[pi % 3], pb[tp][g], o[d][g]);
+        for (int g = 0; g < MLA_BW; g++) o[d][g] = mfma32x32x16_bf16(vop, pb[tp][g], o[d][g]);
         if (pi == 0) {
           mx = s[0];
 #pragma unroll
@@ -733,15 +831,26 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
           neg = -m_use * c;
           grow_own[(t & 1) * 64 * MLA_BW] = __builtin_amdgcn_ballot_w64(mx * c + neg > kMlaGrow) != 0;
         } else if (pi < 6) {
+          f32x4_t r4{};
+          if constexpr (E8) r4 = lds_f32x4(rscale + 32 * (pi - 2));  // read again: fewer live registers
 #pragma unroll
-          for (int v = 0; v < 4; v++) s[4 * (pi - 2) + v] = exp2_fast(fmaf(s[4 * (pi - 2) + v], c, neg));
+          for (int v = 0; v < 4; v++) {
+            const int r = 4 * (pi - 2) + v;
+            s[r] = exp2_fast(fmaf(s[r], c, neg));
+            if constexpr (E8) {  // the weight sums unscaled; P^T carries the value scale
+              l += s[r];
+              s[r] *= r4[v];
+            }
+          }
         } else if (pi == 6) {
 #pragma unroll
           for (int tp2 = 0; tp2 < 2; tp2++) {
             pw[tp2] = i32x4_t{pack_bf16(s[8 * tp2], s[8 * tp2 + 1]), pack_bf16(s[8 * tp2 + 2], s[8 * tp2 + 3]),
                               pack_bf16(s[8 * tp2 + 4], s[8 * tp2 + 5]), pack_bf16(s[8 * tp2 + 6], s[8 * tp2 + 7])};
+            if constexpr (!E8) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) l = dot2_bf16(pw[tp2][i], kBf16PairOne, l);
+              for (int i = 0; i < 4; i++) l = dot2_bf16(pw[tp2][i], kBf16PairOne, l);
+            }
           }
         } else {
 #pragma unroll
@@ -791,204 +900,6 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
     }
   }
 
-}
-
-// ------------------------------------------------------------------------------------
-// MLA decode split over an e4m3 latent cache with one fp32 scale per cache row
-// (kv_scale [B, max_len]; the row serves as K and, through its first 512 columns, as V, so
-// K = code * scale and V = code[:512] * scale).  Same wave-pair layout as the bf16 kernel
-// at half the bytes per key:
-//  * LDS rows are the 576 code bytes, unpadded; 16-byte chunk q of row r sits at chunk
-//    q ^ ((r >> 2) & 3) (within its aligned group of four), which keeps both read
-//    patterns below free of bank conflicts;
-//  * S^T A operand: one 16-byte read gives a lane 16 consecutive latent columns, i.e. its
-//    halves of two 32x32x16 steps (the contraction order is permuted: block p, lane half
-//    hl, step u, element i is column 32p + 16hl + 8u + i, and Q^T uses the same order);
-//    the pair splits the blocks p by parity;
-//  * V^T A operand: one ds_read_b64_tr_b8 per product (8 keys of one column per lane);
-//  * codes convert exactly to bf16; the row scale multiplies S and is folded into P.
-
-constexpr int M8_ROWB = 576;                         // e4m3 latent row
-constexpr int M8_TILE = TK * M8_ROWB;                // 18 KiB per stage
-constexpr int M8_BLKS = M8_TILE / 1024;              // 18 one-KiB direct copies per tile
-constexpr int M8_OPS = (M8_BLKS + MLA_NW - 1) / MLA_NW;  // 3 per wave (wave 2's third: the scales)
-constexpr int M8_SC = 256;                           // scale copy: 64 lanes x 4 bytes
-constexpr int M8_STAGE = M8_TILE + M8_SC;
-constexpr int M8_KR = MLA_DK / 32 / 2;               // 16-byte K reads per wave per tile (9)
-
-__device__ __forceinline__ uint32_t m8_chunk(uint32_t row, uint32_t q) { return q ^ ((row >> 2) & 3u); }
-
-__global__ __launch_bounds__(512, 1) void mla_decode_split_fp8(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) char st0_raw[M8_STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1_raw[M8_STAGE];
-  __shared__ __attribute__((aligned(1024))) char xs_raw[MLA_NW * 4096];  // partial S^T per wave
-  FA_LDS char* const st[MLA_NS] = {(FA_LDS char*)st0_raw, (FA_LDS char*)st1_raw};
-
-  int split, b;
-  if (!mla_item(a, split, b)) return;  // uniform over the workgroup
-  const int L = min(max(a.kv_lens[b], 0), a.max_len);
-  const int start = split * a.chunk;
-  if (start >= L) return;  // uniform over the workgroup
-  const int end = min(start + a.chunk, L);
-  const int n_tiles = (end - start + TK - 1) / TK;
-
-  const int wave = wave_id(), lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
-  const int hh = wave >> 2;
-  const int h = 32 * (wave & 3) + l32;
-  const bool hvalid = h < a.Hq;
-  const float c = a.scale * kLog2e;
-
-  // Q^T half as the B operand: block p = 2i + hh, step u: latent columns 32p + 16hl + 8u .. +7
-  i32x4_t qf[M8_KR][2];
-  {
-    const char* qp = (const char*)a.q + ((size_t)b * a.Hq + (hvalid ? h : 0)) * (MLA_DK * 2);
-#pragma unroll
-    for (int i = 0; i < M8_KR; i++)
-#pragma unroll
-      for (int u = 0; u < 2; u++) qf[i][u] = *(const i32x4_t*)(qp + (32 * (2 * i + hh) + 16 * hl + 8 * u) * 2);
-  }
-  const char* kv = (const char*)a.k + (size_t)b * a.max_len * M8_ROWB;
-  const float* ksb = a.k_scale + (size_t)b * a.max_len;
-  // direct copies of a tile: block blk < 18 of LDS bytes [1024 blk, +1024) is row o / 576,
-  // physical chunk (o % 576) / 16 for o = 1024 blk + 16 lane; wave 2 also brings the tile's
-  // row scales.  Issued from inline asm: the compiler, unable to tell which stage a copy
-  // writes, would otherwise wait for the copies of the next tile before this tile's LDS
-  // reads; each tile starts with an explicit wait for every copy and a barrier instead.
-  auto issue = [&](int t, FA_LDS char* dst) {
-    const int key0 = start + t * TK, valid = min(TK, end - key0);
-    const i32x4_t r = rsrc_words(kv + (size_t)key0 * M8_ROWB, (uint32_t)valid * M8_ROWB);
-    const uint32_t dst_lds = lds_addr(dst);
-#pragma unroll
-    for (int i = 0; i < M8_OPS; i++) {
-      const int blk = i * MLA_NW + wave;
-      if (blk < M8_BLKS) {
-        const uint32_t o = blk * 1024 + lane * 16;
-        const uint32_t row = o / M8_ROWB, pc = (o % M8_ROWB) >> 4;
-        const uint32_t rc = min(row, (uint32_t)(valid - 1));  // rows past the sequence repeat its last row
-        dma16_asm(r, dst_lds + blk * 1024, rc * M8_ROWB + m8_chunk(row, pc) * 16);
-      } else if (blk == M8_BLKS) {
-        const i32x4_t rs = rsrc_words(ksb + key0, (uint32_t)valid * 4);
-        dma4_asm(rs, dst_lds + M8_TILE, (uint32_t)min(lane, valid - 1) * 4);
-      }
-    }
-  };
-  // S^T A operand: key row l32, logical chunk 4i + 2hh + hl; the XOR touches only the two
-  // low chunk bits, so read i sits at one base plus 64i bytes
-  const uint32_t kaddr = l32 * M8_ROWB + (((2 * hh + hl) ^ ((l32 >> 2) & 3)) << 4);
-  // V^T reads: 16-lane group G = lane / 16 (hl = G / 2, column half dh = G % 2); lane 2e + h
-  // of the group reads key row 16tp + 8(e/4) + 4hl + e%4 at byte 8h of chunk
-  // 16hh + 2db + dh, so output byte e of lane l is column 256hh + 32db + l%32 of that key
-  // (16hh + 4(db/2) + dh + 2(db%2) after the XOR: one base per key step and block parity
-  // plus 64(db/2) bytes)
-  uint32_t vaddr[2][2];
-  {
-    const uint32_t G = lane >> 4, e = (lane & 15) >> 1, hb = lane & 1;
-#pragma unroll
-    for (int tp = 0; tp < 2; tp++) {
-      const uint32_t row = 16 * tp + 8 * (e >> 2) + 4 * (G >> 1) + (e & 3);
-      const uint32_t x = (G & 1) ^ ((row >> 2) & 3);
-      vaddr[tp][0] = row * M8_ROWB + 8 * hb + ((16 * hh + x) << 4);
-      vaddr[tp][1] = row * M8_ROWB + 8 * hb + ((16 * hh + (x ^ 2)) << 4);
-    }
-  }
-
-  float m_ref = -INFINITY, neg = 0.f, l = 0.f;
-  f32x16_t o[MLA_DB];
-#pragma unroll
-  for (int d = 0; d < MLA_DB; d++) o[d] = f32x16_t{};
-  FA_LDS char* const xs_own = (FA_LDS char*)xs_raw + wave * 4096 + lane * 16;
-  const FA_LDS char* const xs_peer = (FA_LDS char*)xs_raw + (wave ^ 4) * 4096 + lane * 16;
-
-  auto tile = [&](auto SLOT, int t) {
-    constexpr int sl = decltype(SLOT)::value;
-    wait_vmcnt<0>();  // two stages, as in the bf16 kernel
-    barrier();
-    if (t + 1 < n_tiles) issue(t + 1, st[sl ^ 1]);
-    const FA_LDS char* kt = st[sl];
-    f32x16_t s{};
-#pragma unroll
-    for (int i = 0; i < M8_KR; i++) {
-      const i32x4_t w = lds_b128(kt + kaddr + 64 * i);
-      s = mfma32x32x16_bf16(e4m3x8_to_bf16(i32x2_t{w.x, w.y}), qf[i][0], s);
-      s = mfma32x32x16_bf16(e4m3x8_to_bf16(i32x2_t{w.z, w.w}), qf[i][1], s);
-      if (i % 3 == 2) __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) *(FA_LDS f32x4_t*)(xs_own + 1024 * j) = f32x4_t{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
-    barrier();
-    // register v holds key 8(v/4) + 4hl + v%4 of the tile; its row scale scales S and P
-    f32x4_t sc[4];
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const f32x4_t pv = lds_f32x4(xs_peer + 1024 * j);
-      sc[j] = lds_f32x4(kt + M8_TILE + (8 * j + 4 * hl) * 4);
-#pragma unroll
-      for (int v = 0; v < 4; v++) s[4 * j + v] = (s[4 * j + v] + pv[v]) * sc[j][v];
-    }
-    const int key0 = start + t * TK;
-    if (key0 + TK > end) {
-      const int lim = end - key0 - 4 * hl;
-#pragma unroll
-      for (int v = 0; v < 16; v++) s[v] = (8 * (v >> 2) + (v & 3)) < lim ? s[v] : -INFINITY;
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int v = 1; v < 16; v++) mx = fmaxf(mx, s[v]);
-    mx = xor32_max(mx);
-    if (__builtin_amdgcn_ballot_w64(mx * c > m_ref * c + 8.f)) {  // lazy rescale (P <= 2^8)
-      const float m_new = fmaxf(m_ref, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast((m_ref - m_use) * c);
-      l *= alpha;
-#pragma unroll
-      for (int d = 0; d < MLA_DB; d++) o[d] *= alpha;
-      m_ref = m_new;
-      neg = -m_use * c;
-    }
-    i32x4_t pb[2];
-#pragma unroll
-    for (int tp = 0; tp < 2; tp++) {
-      float e[8];
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        e[i] = exp2_fast(fmaf(s[8 * tp + i], c, neg));
-        l += e[i];
-      }
-      const f32x4_t s0 = sc[2 * tp], s1 = sc[2 * tp + 1];
-      pb[tp] = i32x4_t{pack_bf16(e[0] * s0[0], e[1] * s0[1]), pack_bf16(e[2] * s0[2], e[3] * s0[3]),
-                       pack_bf16(e[4] * s1[0], e[5] * s1[1]), pack_bf16(e[6] * s1[2], e[7] * s1[3])};
-    }
-#pragma unroll
-    for (int tp = 0; tp < 2; tp++)
-#pragma unroll
-      for (int db = 0; db < MLA_DB; db++) {
-        const i32x2_t w = lds_tr8(kt + vaddr[tp][db & 1] + 64 * (db >> 1));
-        o[db] = mfma32x32x16_bf16(e4m3x8_to_bf16(w), pb[tp], o[db]);
-        if (db % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-      }
-  };
-
-  issue(0, st[0]);
-  for (int t = 0; t < n_tiles; t += 2) {
-    tile(std::integral_constant<int, 0>{}, t);
-    if (t + 1 >= n_tiles) break;
-    tile(std::integral_constant<int, 1>{}, t + 1);
-  }
-
-  const float l_tot = xor32_sum(l);
-  if (hvalid) {
-    const size_t pidx = ((size_t)b * a.Hq + h) * a.n_split + split;
-    float* po = a.part_o + pidx * MLA_DV + 256 * hh + 4 * hl;
-#pragma unroll
-    for (int db = 0; db < MLA_DB; db++)
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        *(f32x4_t*)(po + 32 * db + 8 * j) = f32x4_t{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
-    if (hh == 0 && hl == 0) {
-      a.part_ml[2 * pidx] = m_ref;
-      a.part_ml[2 * pidx + 1] = l_tot;
-    }
-  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -1112,8 +1023,8 @@ hipError_t launch_gqa_decode_static(DecodeArgs a, int D, bool fp8, hipStream_t s
 
 hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
   const int grid = a.n_split * ((a.B + 7) / 8 * 8);  // see mla_item
-  if (fp8) mla_decode_split_fp8<<<grid, 64 * MLA_NW, 0, s>>>(a);
-  else mla_decode_split<<<grid, 64 * MLA_BW, 0, s>>>(a);
+  if (fp8) mla_decode_split<true><<<grid, 64 * MLA_BW, 0, s>>>(a);
+  else mla_decode_split<false><<<grid, 64 * MLA_BW, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   combine_kernel<<<(a.B * a.Hq * (MLA_DV / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, MLA_DV);
