@@ -787,17 +787,14 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
       // exponentials, bf16 P^T with its row sum, P^T into the slot of tile t
       const FA_LDS char* vt = ring + stp * STAGE;
       const int u = (t - 1) & 1;
+      // the growth flags of tile t-1 first, so that the branch on them waits for that read
+      // alone; the P^T operands and the first V^T operands are in flight meanwhile
+      const i32x4_t gflag = *(const FA_LDS i32x4_t*)&grow_s[(t - 1) & 1][0][0];
       i32x4_t pb[2][MLA_BW];
 #pragma unroll
       for (int tp = 0; tp < 2; tp++)
 #pragma unroll
         for (int g = 0; g < MLA_BW; g++) pb[tp][g] = lds_b128(pt + (u * 2 * MLA_BW + 2 * g + tp) * 1024 + lane * 16);
-      // tile t-1 outgrew the reference: pass again (its product has not been taken)
-      const i32x4_t gflag = *(const FA_LDS i32x4_t*)&grow_s[(t - 1) & 1][0][0];
-      if (gflag[0] | gflag[1] | gflag[2] | gflag[3]) {  // uniform over the workgroup; rare
-        grew = true;
-        break;
-      }
       // V^T operands as read (e4m3: the eight codes, converted at their products)
       using VRaw = std::conditional_t<E8, i32x2_t, i32x4_t>;
       auto vread = [&](int pi) -> VRaw {
@@ -805,12 +802,17 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
         if constexpr (E8) return lds_tr8(vt + voff[tp][d & 1] + 64 * (d >> 1));
         else return cat(lds_tr16(vt + voff[tp][0] + 2048 * d), lds_tr16(vt + voff[tp][1] + 2048 * d));
       };
-
-      float neg = 0.f;
-      i32x4_t pw[2];
       VRaw va[3];
       va[0] = vread(0);
       va[1] = vread(1);
+      // tile t-1 outgrew the reference: pass again (its product has not been taken)
+      if (gflag[0] | gflag[1] | gflag[2] | gflag[3]) {  // uniform over the workgroup; rare
+        grew = true;
+        break;
+      }
+
+      float neg = 0.f;
+      i32x4_t pw[2];
 #pragma unroll
       for (int pi = 0; pi < 2 * MLA_OB; pi++) {
         if (pi + 2 < 2 * MLA_OB) va[(pi + 2) % 3] = vread(pi + 2);
