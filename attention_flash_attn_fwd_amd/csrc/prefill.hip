@@ -314,16 +314,16 @@ struct VBf16 {
 // read per product) and converted to bf16 exactly; the scale is folded into P, so
 // O^T += V_code^T . (P . v_scale)^T runs on the bf16 matrix cores.
 // V part of a stage: codes [BN][DV] | v_scale [BN] fp32.
-template <int DV_>
+template <int DV_, int NW_ = 4>
 struct VE4m3 {
-  static constexpr int NW = 4;
+  static constexpr int NW = NW_;
   static constexpr int DV = DV_;
   static constexpr int ROWB = DV;
   static constexpr int VS = BN * ROWB;
   static constexpr int BYTES = VS + BN * 4;
   static constexpr bool SCALED = true;
   struct Lane {
-    RowDma<ROWB, SwzV8> dma;
+    RowDma<ROWB, SwzV8, NW_> dma;
     uint32_t va[DV / 32];
     uint32_t sa;
   };
@@ -641,13 +641,14 @@ void launch_mla(const PrefillArgs& a, int grid, int nqb, hipStream_t s) {
 
 hipError_t launch_mla_prefill(const PrefillArgs& a, bool nope_fp8, bool v_fp8, hipStream_t s) {
   int nqb;
-  // e4m3 nope with bf16 V, causal, from 2048 query rows: 8 waves and 256 query rows per
-  // workgroup, sharing each K/V tile copy between twice the rows (as the bf16 prefill)
-  const bool wide = nope_fp8 && !v_fp8 && a.causal && a.Sq >= 2048;
+  // e4m3 nope, causal, from 2048 query rows: 8 waves and 256 query rows per workgroup,
+  // sharing each K/V tile copy between twice the rows (as the bf16 prefill)
+  const bool wide = nope_fp8 && a.causal && a.Sq >= 2048;
   const int grid = items(a, wide ? 256 : 128, nqb);
   if (grid == 0) return hipSuccess;
   if (wide) {
-    launch_mla<QkMla<true, 8>, VBf16<128, 8>>(a, grid, nqb, s);
+    if (v_fp8) launch_mla<QkMla<true, 8>, VE4m3<128, 8>>(a, grid, nqb, s);
+    else launch_mla<QkMla<true, 8>, VBf16<128, 8>>(a, grid, nqb, s);
   } else if (nope_fp8) {
     if (v_fp8) launch_mla<QkMla<true>, VE4m3<128>>(a, grid, nqb, s);
     else launch_mla<QkMla<true>, VBf16<128>>(a, grid, nqb, s);

@@ -187,6 +187,7 @@ MLA_BATCHED = [
     (2, 96, 257, 2, 1, True, False, False, True),     # e4m3 nope without scales
     (2, 300, 300, 2, 1, True, True, False, True),     # Sq = Skv across two sequences
     (2, 2080, 2200, 2, 1, True, True, False, True),   # long causal rows: 256-row blocks, ragged tail
+    (1, 2300, 2100, 2, 2, True, True, True, True),    # the same with e4m3 V, Sq > Skv
 ]
 
 
