@@ -912,7 +912,8 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
 // Combine: merges, for every (batch, head) row, the splits that cover [0, L_b) in split
 // order (deterministic, no atomics): O = sum_s w_s O_s / sum_s w_s l_s with
 // w_s = exp2((m_s - M) c), M = max_s m_s.  A thread owns 8 consecutive output columns of
-// one row, so its loads of the partials are independent 16-byte reads.
+// one row, so its loads of the partials are independent 16-byte reads, non-temporal (read
+// once).
 
 constexpr int CMB_COLS = 8;
 
@@ -935,8 +936,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
   for (int s = 0; s < ns; s++) {
     const float w = exp2_fast((ml[2 * s] - M) * c);
     den = fmaf(w, ml[2 * s + 1], den);
-    const f32x4_t u0 = *(const f32x4_t*)(po + (size_t)s * Dv);
-    const f32x4_t u1 = *(const f32x4_t*)(po + (size_t)s * Dv + 4);
+    const f32x4_t u0 = __builtin_nontemporal_load((const f32x4_t*)(po + (size_t)s * Dv));
+    const f32x4_t u1 = __builtin_nontemporal_load((const f32x4_t*)(po + (size_t)s * Dv + 4));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       x0[i] = fmaf(w, u0[i], x0[i]);
