@@ -637,7 +637,11 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
     if constexpr (E8) {
       const int j = 4 * k + wave;  // wave-uniform
       if (j < M8_BLKS) {
-        const uint32_t o = 1024u * j + 16u * lane, row = o / M8_ROWB, pc = (o % M8_ROWB) >> 4;
+        // the lane's source offset from a fresh lane index (an asm the compiler cannot hoist):
+        // offsets precomputed for every copy would stay live across the tile loop
+        uint32_t lane_c;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_c));
+        const uint32_t o = 1024u * j + 16u * lane_c, row = o / M8_ROWB, pc = (o % M8_ROWB) >> 4;
         const uint32_t src = min(row, (uint32_t)(cp.valid - 1)) * M8_ROWB + m8_chunk(row, pc) * 16;
         dma16_asm(cp.r, cp.dst + 1024u * j, cp.live ? src : kOutOfRange);
       } else if (j == M8_BLKS) {
@@ -782,7 +786,11 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
       const int key0 = start + t * TK;
       if (key0 + TK > end) {  // the last tiles only: a branch, not selects on every tile
         asm volatile("" ::: "memory");
-        const int lim = end - key0 - 4 * hl;
+        // the lane half from a fresh lane index (an asm the compiler cannot hoist), so that no
+        // per-lane limit stays live across the tile loop
+        int lane_m;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_m));
+        const int lim = end - key0 - 4 * (lane_m >> 5);
 #pragma unroll
         for (int v = 0; v < 16; v++) s[v] = (8 * (v >> 2) + (v & 3)) < lim ? s[v] : -INFINITY;
       }
