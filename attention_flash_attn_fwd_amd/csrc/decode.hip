@@ -552,6 +552,26 @@ constexpr int M8_TILE = TK * M8_ROWB;                 // 18 KiB of codes per til
 constexpr int M8_BLKS = M8_TILE / 1024;               // 18 one-KiB direct copies per tile
 constexpr int M8_STAGE = M8_TILE + 256;               // codes | row scales
 constexpr int M8_CPW = 5;                             // direct copies per wave per tile, e4m3
+
+// Split partials of the MLA O in three bytes per value: the upper three bytes of the fp32 value
+// (sign, exponent, 15 of its 23 mantissa bits; truncation, so a relative error below 2^-15,
+// against the 2^-9 of the bf16 output), rows of MLA_DV * 3 bytes.  Every split writes 64 MiB of
+// fp32 partials at B64 H128 and the combine reads them back; three bytes cut both by a quarter.
+constexpr int MLA_PB = 3;  // bytes per partial O value
+typedef int i32x3_a4 __attribute__((ext_vector_type(3))) __attribute__((aligned(4)));
+__device__ __forceinline__ i32x3_a4 pack_f24x4(float x0, float x1, float x2, float x3) {
+  const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1), b2 = __float_as_uint(x2),
+                 b3 = __float_as_uint(x3);
+  // byte stream: b0[1..3] b1[1..3] b2[1..3] b3[1..3] (v_perm_b32: selector values 0-3 pick the
+  // bytes of the second operand, 4-7 those of the first)
+  return i32x3_a4{(int)__builtin_amdgcn_perm(b1, b0, 0x05030201u), (int)__builtin_amdgcn_perm(b2, b1, 0x06050302u),
+                  (int)__builtin_amdgcn_perm(b3, b2, 0x07060503u)};
+}
+__device__ __forceinline__ f32x4_t unpack_f24x4(i32x3_a4 w) {
+  const uint32_t w0 = (uint32_t)w.x, w1 = (uint32_t)w.y, w2 = (uint32_t)w.z;
+  return f32x4_t{__uint_as_float(w0 << 8), __uint_as_float(((w0 >> 16) | (w1 << 16)) & 0xFFFFFF00u),
+                 __uint_as_float(((w1 >> 8) | (w2 << 24)) & 0xFFFFFF00u), __uint_as_float(w2 & 0xFFFFFF00u)};
+}
 static_assert(M8_BLKS + 1 <= M8_CPW * MLA_BW && 2 * M8_CPW - 1 <= MLA_QS / 4,
               "the copies cover codes and scales, one per second group of four S steps");
 
@@ -714,8 +734,12 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
       const Copy c0 = plan_copy(0, 0);
 #pragma unroll
       for (int k = 0; k < (E8 ? M8_CPW : MLA_CPW); k++) copy(c0, k);
+      // the zeros from an asm the compiler cannot hoist: a zero vector kept in registers across
+      // the passes was spilled
+      int z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
 #pragma unroll
-      for (int tp = 0; tp < 2; tp++) *(FA_LDS i32x4_t*)(pt + (2 * MLA_BW + 2 * wave + tp) * 1024 + lane * 16) = i32x4_t{0, 0, 0, 0};
+      for (int tp = 0; tp < 2; tp++) *(FA_LDS i32x4_t*)(pt + (2 * MLA_BW + 2 * wave + tp) * 1024 + lane * 16) = i32x4_t{z, z, z, z};
       grow_own[64 * MLA_BW] = 0;  // tile "-1" (parity 1)
     }
     int stc = 0;
@@ -905,12 +929,13 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
     const int hg = 32 * g + l32e;
     if (hg < a.Hq) {
       const size_t pidx = ((size_t)b * a.Hq + hg) * a.n_split + split;
-      float* po = a.part_o + pidx * MLA_DV + 128 * wave + 4 * hle;
+      char* po = (char*)a.part_o + (pidx * MLA_DV + 128 * wave + 4 * hle) * MLA_PB;
 #pragma unroll
       for (int d = 0; d < MLA_OB; d++)
 #pragma unroll
         for (int j = 0; j < 4; j++)
-          *(f32x4_t*)(po + 32 * d + 8 * j) = f32x4_t{o[d][g][4 * j], o[d][g][4 * j + 1], o[d][g][4 * j + 2], o[d][g][4 * j + 3]};
+          *(i32x3_a4*)(po + (32 * d + 8 * j) * MLA_PB) =
+              pack_f24x4(o[d][g][4 * j], o[d][g][4 * j + 1], o[d][g][4 * j + 2], o[d][g][4 * j + 3]);
     }
   }
 
@@ -920,11 +945,12 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
 // Combine: merges, for every (batch, head) row, the splits that cover [0, L_b) in split
 // order (deterministic, no atomics): O = sum_s w_s O_s / sum_s w_s l_s with
 // w_s = exp2((m_s - M) c), M = max_s m_s.  A thread owns 8 consecutive output columns of
-// one row, so its loads of the partials are independent 16-byte reads, non-temporal (read
-// once).
+// one row, so its loads of the partials are independent reads, non-temporal (read once).
+// PB: bytes per partial O value (4: fp32, the GQA splits; MLA_PB: the MLA splits).
 
 constexpr int CMB_COLS = 8;
 
+template <int PB>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
   const int tpr = Dv / CMB_COLS;  // threads per row
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
@@ -935,7 +961,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
   const int ns = (L + a.chunk - 1) / a.chunk;
   const float c = a.scale * kLog2e;
   const float* ml = a.part_ml + (size_t)bh * a.n_split * 2;
-  const float* po = a.part_o + (size_t)bh * a.n_split * Dv + d0;
+  const char* po = (const char*)a.part_o + ((size_t)bh * a.n_split * Dv + d0) * PB;
   float M = -INFINITY;
   for (int s = 0; s < ns; s++) M = fmaxf(M, ml[2 * s]);
   float den = 0.f;
@@ -944,8 +970,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
   for (int s = 0; s < ns; s++) {
     const float w = exp2_fast((ml[2 * s] - M) * c);
     den = fmaf(w, ml[2 * s + 1], den);
-    const f32x4_t u0 = __builtin_nontemporal_load((const f32x4_t*)(po + (size_t)s * Dv));
-    const f32x4_t u1 = __builtin_nontemporal_load((const f32x4_t*)(po + (size_t)s * Dv + 4));
+    const char* ps = po + (size_t)s * Dv * PB;
+    f32x4_t u0, u1;
+    if constexpr (PB == 4) {
+      u0 = __builtin_nontemporal_load((const f32x4_t*)ps);
+      u1 = __builtin_nontemporal_load((const f32x4_t*)ps + 1);
+    } else {
+      static_assert(PB == MLA_PB, "partial format");
+      u0 = unpack_f24x4(__builtin_nontemporal_load((const i32x3_a4*)ps));
+      u1 = unpack_f24x4(__builtin_nontemporal_load((const i32x3_a4*)(ps + 12)));
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       x0[i] = fmaf(w, u0[i], x0[i]);
@@ -983,7 +1017,7 @@ hipError_t launch_gqa_decode(const DecodeArgs& a, int D, bool fp8, hipStream_t s
                : D == 64  ? launch_gqa_split<64>(a, fp8, grid, s)
                           : hipErrorInvalidValue;
   if (e != hipSuccess) return e;
-  combine_kernel<<<(a.B * a.Hq * (D / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, D);
+  combine_kernel<4><<<(a.B * a.Hq * (D / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, D);
   return hipGetLastError();
 }
 
@@ -1042,7 +1076,7 @@ hipError_t launch_mla_decode(const DecodeArgs& a, bool fp8, hipStream_t s) {
   else mla_decode_split<false><<<grid, 64 * MLA_BW, 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_kernel<<<(a.B * a.Hq * (MLA_DV / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, MLA_DV);
+  combine_kernel<MLA_PB><<<(a.B * a.Hq * (MLA_DV / CMB_COLS) + 255) / 256, 256, 0, s>>>(a, MLA_DV);
   return hipGetLastError();
 }
 
