@@ -43,6 +43,26 @@ def test_fp32_ragged(causal, D):
     _check_full(w, F32_TOL)
 
 
+F32_CASES = [
+    # B, Sq, Skv, Hq, Hkv, D, causal -- fewer than 256 blocks of 128 rows: 32-row blocks whose
+    # four waves split the key tiles
+    (1, 77, 333, 4, 4, 64, True),       # Sq < Skv: bottom-right causal
+    (1, 200, 50, 2, 1, 128, True),      # Sq > Skv: leading rows see no key
+    (2, 40, 1000, 4, 1, 64, False),     # several tiles per wave, GQA
+    (1, 1, 517, 2, 2, 128, False),      # one query row
+    (1, 5, 7, 1, 1, 64, True),          # smaller than one tile
+    # 256 blocks of 128 rows or more: the LDS-staged kernel
+    (4, 1100, 1100, 8, 4, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,Sq,Skv,Hq,Hkv,D,causal", F32_CASES)
+def test_fp32_shapes(B, Sq, Skv, Hq, Hkv, D, causal):
+    w = workload("mha_fp32_b1_h4_s128_d64", B=B, Sq=Sq, Skv=Skv, Hq=Hq, Hkv=Hkv, D=D, Dv=D, causal=causal,
+                 scale=D ** -0.5)
+    _check_full(w, F32_TOL)
+
+
 BF16_CASES = [
     # B, Sq, Skv, Hq, Hkv, D, causal
     (2, 300, 300, 4, 2, 128, False),
