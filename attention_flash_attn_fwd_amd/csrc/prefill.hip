@@ -99,6 +99,7 @@ template <int D, int NW_ = 4>
 struct QkBf16 {
   static constexpr int NW = NW_;  // waves of the workgroup that share the copies
   static constexpr bool REV_SECOND = false;  // key order of a causal pair's second block
+  static constexpr bool STAGE_O = false;     // O rows staged through LDS for whole-row stores
   static constexpr int ROWB = D * 2;
   static constexpr int KBYTES = BN * ROWB;
   struct QFrag {
@@ -142,6 +143,7 @@ template <bool FP8, int NW_ = 4>
 struct QkMla {
   static constexpr int NW = NW_;  // waves of the workgroup that share the copies
   static constexpr bool REV_SECOND = true;  // key order of a causal pair's second block
+  static constexpr bool STAGE_O = FP8;      // O rows staged through LDS for whole-row stores
   static constexpr int NROWB = FP8 ? 128 : 256;
   static constexpr int KN = 0;
   static constexpr int KR = BN * NROWB;
@@ -575,7 +577,36 @@ __global__ __launch_bounds__(64 * QK::NW, 2) void prefill_kernel(PrefillArgs pa,
     // epilogue: O = O^T / l, LSE = m_ref * scale + ln l
     const float l_tot = xor32_sum(st.l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < p.Sq) {
+    constexpr bool STAGE_O = QK::STAGE_O && DV == 128 && 4 * 32 * OROWB <= STAGE;
+    if constexpr (STAGE_O) {
+      // MLA with e4m3 nope and bf16 V: O goes through LDS so that each store instruction writes
+      // four whole 256-byte rows.  Stored straight from the O^T layout, each store writes 16
+      // bytes of each of 32 rows, and lines that left L2 partly written were written back more
+      // than once (1.7x the output bytes on B1 H128 S8192, where K/V fill L2; 1 % faster
+      // staged).  This wave's 32 rows: 16-byte chunk c of row r at chunk c ^ (r & 15) (the
+      // writes of 16 rows then cover all banks).  The e4m3-V stage is too small for four
+      // waves' rows, and the bf16 MHA kernels' output lines are written once as they are.
+      barrier();  // every wave is done with both stages, and no copy is in flight
+      FA_LDS char* ow = (wave < 4 ? stage0 : stage1) + (wave & 3) * (32 * OROWB);
+#pragma unroll
+      for (int db = 0; db < DV / 32; db++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int ch = 4 * db + j;
+          *(FA_LDS i32x2_t*)(ow + l32 * OROWB + ((ch ^ (l32 & 15)) << 4) + 8 * hl) =
+              i32x2_t{pack_bf16(st.o[db][4 * j] * inv, st.o[db][4 * j + 1] * inv),
+                      pack_bf16(st.o[db][4 * j + 2] * inv, st.o[db][4 * j + 3] * inv)};
+        }
+#pragma unroll
+      for (int k = 0; k < 8; k++) {
+        const int r = 4 * k + (lane >> 4), ch = lane & 15;
+        const i32x4_t x = *(const FA_LDS i32x4_t*)(ow + r * OROWB + ((ch ^ (r & 15)) << 4));
+        if (wrow0 + r < p.Sq)
+          *(i32x4_t*)((char*)p.o + (((size_t)b * p.Sq + wrow0 + r) * p.Hq + h) * (size_t)OROWB + ch * 16) = x;
+      }
+      if (p.lse && hl == 0 && qrow < p.Sq)
+        p.lse[lse_off + h * lse_hs + qrow] = l_tot > 0.f ? st.m_ref * p.scale + logf(l_tot) : -INFINITY;
+    } else if (qrow < p.Sq) {
       char* ob = (char*)p.o + (((size_t)b * p.Sq + qrow) * p.Hq + h) * (size_t)OROWB;
 #pragma unroll
       for (int db = 0; db < DV / 32; db++)
