@@ -63,6 +63,18 @@ def test_fp32_shapes(B, Sq, Skv, Hq, Hkv, D, causal):
     _check_full(w, F32_TOL)
 
 
+def test_fp32_deterministic():
+    """The key-split fp32 kernel merges its waves' partial results in a fixed order: two calls
+    give the same bits."""
+    w = workload("mha_fp32_b1_h4_s128_d64", B=2, Sq=70, Skv=900, Hq=4, Hkv=2, causal=True)
+    q, k, v = _inputs(w)
+    a = fa.prefill(q, k, v, causal=True, return_lse=True)
+    b = fa.prefill(q, k, v, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int32), b[0].view(torch.int32))
+    assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
 BF16_CASES = [
     # B, Sq, Skv, Hq, Hkv, D, causal
     (2, 300, 300, 4, 2, 128, False),
