@@ -162,6 +162,7 @@ struct QkMla {
     uint32_t na[NNA];  // nope chunk offsets
     uint32_t ra[4];    // rope chunk offsets
     uint32_t sa;       // k_scale offset of this lane's first key
+    uint32_t sf;       // k_scale offset of key l32 of a 32-key block
   };
 
   __device__ static void init(const PrefillArgs& p, int wave, int lane, Lane& s) {
@@ -183,6 +184,7 @@ struct QkMla {
 #pragma unroll
     for (int c = 0; c < 4; c++) s.ra[c] = KR + l32 * 128 + (((2 * c + hl) ^ swr) << 4);
     s.sa = KS + 16 * hl;
+    s.sf = KS + 4 * l32;
   }
   __device__ static void load_q(const PrefillArgs& p, int b, int h, int qrow, int hl, QFrag& q) {
     const size_t tok = ((size_t)b * p.Sq + qrow) * p.Hq + h;
@@ -220,7 +222,12 @@ struct QkMla {
   }
   __device__ static void scores(const QFrag& q, const Lane& s, const FA_LDS char* stage, int kb, int hl,
                                 f32x16_t& acc, bool has_kscale) {
-    (void)hl;
+    // F = k_scale (x) q_scale over the block's 32 keys and 32 rows, in the S^T accumulator
+    // layout, by one fp32 outer-product MFMA (the lanes of half 0 give the key scales and the
+    // row scale, those of half 1 zeros): one rounding per product, as q_scale * k_scale on the
+    // vector ALU, without its 16 multiplies and four scale reads
+    const float kv = has_kscale ? *(const FA_LDS float*)(stage + s.sf + kb * 128) : 1.f;
+    const f32x16_t f = mfma32x32x2_f32(hl ? 0.f : kv, hl ? 0.f : q.qs, f32x16_t{});
     f32x16_t sn{};
     if constexpr (FP8) {
 #pragma unroll
@@ -233,14 +240,9 @@ struct QkMla {
 #pragma unroll
       for (int c = 0; c < 8; c++) sn = mfma32x32x16_bf16(lds_b128(stage + s.na[c] + kb * 32 * NROWB), q.n16[c], sn);
     }
-    // the nope product scaled by q_scale * k_scale in place, then the rope products accumulate
-    // onto it (one accumulator); this lane holds keys 32kb + 8j + 4hl + i in register 4j + i
+    // the nope product scaled in place, then the rope products accumulate onto it
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const f32x4_t ks = has_kscale ? lds_f32x4(stage + s.sa + (32 * kb + 8 * j) * 4) : f32x4_t{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-      for (int i = 0; i < 4; i++) sn[4 * j + i] *= q.qs * ks[i];
-    }
+    for (int v = 0; v < 16; v++) sn[v] *= f[v];
 #pragma unroll
     for (int c = 0; c < 4; c++) sn = mfma32x32x16_bf16(lds_b128(stage + s.ra[c] + kb * 32 * 128), q.r[c], sn);
     acc = sn;
