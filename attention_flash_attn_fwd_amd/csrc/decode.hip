@@ -553,24 +553,19 @@ constexpr int M8_BLKS = M8_TILE / 1024;               // 18 one-KiB direct copie
 constexpr int M8_STAGE = M8_TILE + 256;               // codes | row scales
 constexpr int M8_CPW = 5;                             // direct copies per wave per tile, e4m3
 
-// Split partials of the MLA O in three bytes per value: the upper three bytes of the fp32 value
-// (sign, exponent, 15 of its 23 mantissa bits; truncation, so a relative error below 2^-15,
-// against the 2^-9 of the bf16 output), rows of MLA_DV * 3 bytes.  Every split writes 64 MiB of
-// fp32 partials at B64 H128 and the combine reads them back; three bytes cut both by a quarter.
-constexpr int MLA_PB = 3;  // bytes per partial O value
-typedef int i32x3_a4 __attribute__((ext_vector_type(3))) __attribute__((aligned(4)));
-__device__ __forceinline__ i32x3_a4 pack_f24x4(float x0, float x1, float x2, float x3) {
-  const uint32_t b0 = __float_as_uint(x0), b1 = __float_as_uint(x1), b2 = __float_as_uint(x2),
-                 b3 = __float_as_uint(x3);
-  // byte stream: b0[1..3] b1[1..3] b2[1..3] b3[1..3] (v_perm_b32: selector values 0-3 pick the
-  // bytes of the second operand, 4-7 those of the first)
-  return i32x3_a4{(int)__builtin_amdgcn_perm(b1, b0, 0x05030201u), (int)__builtin_amdgcn_perm(b2, b1, 0x06050302u),
-                  (int)__builtin_amdgcn_perm(b3, b2, 0x07060503u)};
-}
-__device__ __forceinline__ f32x4_t unpack_f24x4(i32x3_a4 w) {
-  const uint32_t w0 = (uint32_t)w.x, w1 = (uint32_t)w.y, w2 = (uint32_t)w.z;
-  return f32x4_t{__uint_as_float(w0 << 8), __uint_as_float(((w0 >> 16) | (w1 << 16)) & 0xFFFFFF00u),
-                 __uint_as_float(((w1 >> 8) | (w2 << 24)) & 0xFFFFFF00u), __uint_as_float(w2 & 0xFFFFFF00u)};
+// Split partials of the MLA O as 16-bit integers with one power-of-two scale per 128-column
+// segment (the columns one wave holds) of each (head, split) row: value = q * 2^(e - 14), with
+// 2^e above the segment's largest magnitude, so |q| < 2^14 and the truncation error is below
+// 2^-13 of that largest magnitude (against the 2^-9 relative rounding of the bf16 output).  The
+// int16 rows (MLA_DV * 2 bytes) are followed by the exponents, [B, H, n_split, MLA_BW] int32.
+// In fp32 the partials are 64 MiB at B64 H128, written by the splits and read back by the
+// combine; two bytes per value halve that.  They fit in the workspace sized for fp32 partials.
+constexpr int MLA_PB = 2;                      // bytes per partial O value
+constexpr int MLA_SEG = MLA_DV / MLA_BW;       // columns per exponent (one wave's share)
+constexpr int kMlaMinExp = -100;               // smaller segment maxima share this exponent
+static_assert(MLA_DV * MLA_PB + 4 * MLA_BW <= MLA_DV * 4, "int16 rows and exponents within the fp32 sizing");
+__device__ __forceinline__ int* mla_part_exps(const DecodeArgs& a) {
+  return (int*)((char*)a.part_o + (size_t)a.B * a.Hq * a.n_split * MLA_DV * MLA_PB);
 }
 static_assert(M8_BLKS + 1 <= M8_CPW * MLA_BW && 2 * M8_CPW - 1 <= MLA_QS / 4,
               "the copies cover codes and scales, one per second group of four S steps");
@@ -926,16 +921,28 @@ __global__ __launch_bounds__(64 * MLA_BW, 1) void mla_decode_split(DecodeArgs a)
   // head 32g + l32
 #pragma unroll
   for (int g = 0; g < MLA_BW; g++) {
+    // the segment (this wave's 128 columns of head 32g + l32) lies in lanes l32 and l32 + 32
+    float mx = 0.f;
+#pragma unroll
+    for (int d = 0; d < MLA_OB; d++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) mx = fmaxf(mx, fabsf(o[d][g][v]));
+    mx = xor32_max(mx);
+    const int e = mx > 0.f ? max(__builtin_amdgcn_frexp_expf(mx), kMlaMinExp) : kMlaMinExp;  // mx < 2^e
+    const float sc = __builtin_amdgcn_ldexpf(1.f, 14 - e);
     const int hg = 32 * g + l32e;
     if (hg < a.Hq) {
       const size_t pidx = ((size_t)b * a.Hq + hg) * a.n_split + split;
-      char* po = (char*)a.part_o + (pidx * MLA_DV + 128 * wave + 4 * hle) * MLA_PB;
+      if (hle == 0) mla_part_exps(a)[pidx * MLA_BW + wave] = e;
+      char* po = (char*)a.part_o + (pidx * MLA_DV + MLA_SEG * wave + 4 * hle) * MLA_PB;
 #pragma unroll
       for (int d = 0; d < MLA_OB; d++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-          *(i32x3_a4*)(po + (32 * d + 8 * j) * MLA_PB) =
-              pack_f24x4(o[d][g][4 * j], o[d][g][4 * j + 1], o[d][g][4 * j + 2], o[d][g][4 * j + 3]);
+        for (int j = 0; j < 4; j++) {
+          const auto lo = __builtin_amdgcn_cvt_pk_i16((int)(o[d][g][4 * j] * sc), (int)(o[d][g][4 * j + 1] * sc));
+          const auto hi = __builtin_amdgcn_cvt_pk_i16((int)(o[d][g][4 * j + 2] * sc), (int)(o[d][g][4 * j + 3] * sc));
+          *(i32x2_t*)(po + (32 * d + 8 * j) * MLA_PB) = i32x2_t{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+        }
     }
   }
 
@@ -977,8 +984,16 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int Dv) {
       u1 = __builtin_nontemporal_load((const f32x4_t*)ps + 1);
     } else {
       static_assert(PB == MLA_PB, "partial format");
-      u0 = unpack_f24x4(__builtin_nontemporal_load((const i32x3_a4*)ps));
-      u1 = unpack_f24x4(__builtin_nontemporal_load((const i32x3_a4*)(ps + 12)));
+      const i32x4_t w = __builtin_nontemporal_load((const i32x4_t*)ps);
+      const int e = mla_part_exps(a)[((size_t)bh * a.n_split + s) * MLA_BW + d0 / MLA_SEG] - 14;
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        // low and high 16-bit halves, sign-extended
+        u0[2 * i] = __builtin_amdgcn_ldexpf((float)(short)w[i], e);
+        u0[2 * i + 1] = __builtin_amdgcn_ldexpf((float)(w[i] >> 16), e);
+        u1[2 * i] = __builtin_amdgcn_ldexpf((float)(short)w[2 + i], e);
+        u1[2 * i + 1] = __builtin_amdgcn_ldexpf((float)(w[2 + i] >> 16), e);
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {

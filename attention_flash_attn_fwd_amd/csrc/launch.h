@@ -40,7 +40,7 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   const float* k_scale; // e4m3 caches: GQA [B, max_len, Hkv] per key row, MLA [B, max_len]; else NULL
   const float* v_scale; // e4m3 GQA cache: [B, max_len, Hkv]; else NULL
-  float* part_o;        // workspace: [B, Hq, n_split, Dv] fp32 (GQA: Dv = D); MLA: 3 bytes per value
+  float* part_o;        // workspace: [B, Hq, n_split, Dv] fp32 (GQA: Dv = D); MLA: int16 + exponents
   float* part_ml;       // workspace: [B, Hq, n_split, 2] fp32 (row max, row sum)
   int B, Hq, Hkv, max_len;
   int n_split, chunk;   // keys per split
