@@ -12,7 +12,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.cpp", "plan.cpp", "prefill.hip", "prefill_w64.hip", "prefill_f32.hip", "decode.hip", "merge.hip", "quantize.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "prefill.hip", "prefill_w64.hip", "prefill_f32.hip", "gqa_decode.hip", "decode.hip",
+           "merge.hip", "quantize.hip"]
+# per-source compiler options: the GQA decode kernels keep their matrix-core accumulators in
+# ordinary vector registers (they need few registers; see the header of gqa_decode.hip)
+EXTRA_FLAGS = {"gqa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
@@ -46,7 +50,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for s in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
-        jobs.append((obj, [cc, "-x", "hip", *HIPCC_FLAGS, "-c", os.path.join(CSRC, s), "-o", obj]))
+        jobs.append((obj, [cc, "-x", "hip", *HIPCC_FLAGS, *EXTRA_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", obj]))
     with ThreadPoolExecutor(len(jobs)) as ex:
         outs = list(ex.map(lambda j: _run(j[1]), jobs))
     tmp = LIB + ".tmp"

@@ -87,6 +87,8 @@ SplitPlan mla_decode_plan(int B, int H, int max_len);
 size_t decode_workspace_bytes(int B, int Hq, int Dv, int n_split);
 
 hipError_t launch_gqa_decode(const DecodeArgs& a, int D, bool fp8, hipStream_t s);
+// The GQA split kernels alone (gqa_decode.hip); launch_gqa_decode adds the combine.
+hipError_t launch_gqa_split_kernels(const DecodeArgs& a, int D, bool fp8, hipStream_t s);
 // The same with the partials in the library's static per-GPU buffer (a.part_o / a.part_ml are
 // set here); the caller has checked that they fit in kDecodeStaticScratchBytes.
 hipError_t launch_gqa_decode_static(DecodeArgs a, int D, bool fp8, hipStream_t s);
