@@ -14,9 +14,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["api.cpp", "plan.cpp", "prefill.hip", "prefill_w64.hip", "prefill_f32.hip", "gqa_decode.hip", "decode.hip",
            "merge.hip", "quantize.hip"]
-# per-source compiler options: the GQA decode kernels keep their matrix-core accumulators in
-# ordinary vector registers (they need few registers; see the header of gqa_decode.hip)
-EXTRA_FLAGS = {"gqa_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# per-source compiler options: the GQA decode and fp32 prefill kernels keep their matrix-core
+# accumulators in ordinary vector registers (they need few registers; see the headers of those
+# sources)
+VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA_FLAGS = {"gqa_decode.hip": VGPR_MFMA, "prefill_f32.hip": VGPR_MFMA}
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

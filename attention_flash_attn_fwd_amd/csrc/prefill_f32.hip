@@ -5,6 +5,10 @@
 // v_mfma_f32_32x32x2_f32 for both products, in the transposed form that lets a lane own one
 // query column (S^T = K.Q^T, O^T = V^T.P^T).  K/V tiles of 32 keys are staged through LDS with
 // ordinary loads, one stage: the fp32 workload is small and latency-bound.
+//
+// This file is compiled with the matrix-core accumulators in ordinary vector registers
+// (-mllvm -amdgpu-mfma-vgpr-form): at head dim 64 the kernels then run four waves per SIMD
+// instead of two or three (5.7 % faster on a causal B4 H8 S1100 D64 call).
 #include "device.h"
 #include "launch.h"
 
