@@ -71,7 +71,9 @@ constexpr int M8_CPW = 5;                             // direct copies per wave 
 // Split partials of the MLA O as 16-bit integers with one power-of-two scale per 128-column
 // segment (the columns one wave holds) of each (head, split) row: value = q * 2^(e - 14), with
 // 2^e above the segment's largest magnitude, so |q| < 2^14 and the truncation error is below
-// 2^-13 of that largest magnitude (against the 2^-9 relative rounding of the bf16 output).  The
+// 2^-13 of that largest magnitude (against the 2^-9 relative rounding of the bf16 output; the
+// bound is absolute within a segment, so a column far below the segment's largest keeps an
+// error relative to that largest value, not to its own).  The
 // int16 rows (MLA_DV * 2 bytes) are followed by the exponents, [B, H, n_split, MLA_BW] int32.
 // In fp32 the partials are 64 MiB at B64 H128, written by the splits and read back by the
 // combine; two bytes per value halve that.  They fit in the workspace sized for fp32 partials.
